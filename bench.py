@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the prefix-shared paged-KV attention path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic
+input, with every input already resident in HBM:
+  admission (radix-tree match / lock / slot allocation) -> page-table and
+  work-list upload -> KV scatter -> extend attention, for every phase (the
+  prefix hints first, then the requests that share them) -> decode steps
+  (allocation, upload, KV scatter, decode attention) -> finish (insert +
+  unlock).  The tree starts empty each step.
+
+Prints ONE JSON line.  `value` = (extend query tokens + decode tokens) per
+step / wall time per step.  Kernel-level rates use per-launch durations from
+HIP events bound to each attention kernel's dispatch (rdx_timing_*), taken
+in the timed region on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
+
+
+def extend_flops(cfg, phase_reqs):
+    """Unmasked (query, key) pairs x 4 D Hq: S*P + S(S+1)/2 per request."""
+    tot = 0
+    for r in phase_reqs:
+        S, P = r.own_len, r.prompt_len - r.own_len
+        tot += S * P + S * (S + 1) // 2
+    return 4 * cfg.head_dim * cfg.n_q_heads * tot
+
+
+def decode_bytes(wl, t):
+    """Algorithmic HBM bytes of decode step t: every distinct KV row read
+    once (shared prefixes once, each request's own rows once) for K and V,
+    its 4-byte page index, the queries and the outputs."""
+    cfg = wl.cfg
+    b = 2 if cfg.dtype == "bf16" else 4
+    leaves = wl.leaf_requests
+    shared = sum(n.length for n in wl.nodes if n.level < cfg.n_levels - 1)
+    own = sum(r.own_len + t + 1 for r in leaves)
+    rows = shared + own
+    kv = rows * 2 * cfg.n_kv_heads * cfg.head_dim * b
+    qo = 2 * len(leaves) * cfg.n_q_heads * cfg.head_dim * b
+    return kv + qo + 4 * rows
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle, untuned, on this host's cores, over a bounded sample: the
+    cache model for the whole workload plus attention for the first leaf
+    requests until `seconds` of attention work have been done."""
+    import numpy as np
+    import oracle
+    from oracle.run import request_attention
+
+    cores = len(os.sched_getaffinity(0))
+    leaves = wl.leaf_requests
+    t0 = time.perf_counter()
+    oracle.run_workload(wl, attention_for=())
+    t_cache = time.perf_counter() - t0
+    done, toks, t_attn = 0, 0, 0.0
+    while done < len(leaves) and t_attn < seconds:
+        r = leaves[done]
+        t1 = time.perf_counter()
+        request_attention(wl, r)
+        t_attn += time.perf_counter() - t1
+        toks += r.own_len + r.decode_steps
+        done += 1
+    # whole-workload tokens / (cache model time + attention time scaled to all leaves)
+    frac = done / max(1, len(leaves))
+    all_toks = sum(r.own_len + r.decode_steps for r in leaves)
+    est = t_cache + t_attn / max(frac, 1e-9)
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": all_toks / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle: cache model over all {len(wl.all_requests)} requests "
+                      f"({t_cache:.2f}s) + attention of the first {done} of {len(leaves)} leaf requests "
+                      f"({t_attn:.2f}s, {toks} query tokens), rate scaled to all leaf tokens; "
+                      f"BLAS threads = host cores; cpu: {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="helpdesk")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extend-items", type=int, default=0)
+    ap.add_argument("--decode-items", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from prefix_shared_kv_token_amd import rdx
+    from prefix_shared_kv_token_amd.driver import WorkloadRun
+    from workloads import Workload, config_by_name
+
+    cfg = config_by_name(args.config)
+    wl = Workload(cfg)
+    print(f"[bench] {cfg.name}: building inputs", file=sys.stderr, flush=True)
+    run = WorkloadRun(wl, extend_items=args.extend_items, decode_items=args.decode_items)
+    for _ in range(args.warmup):
+        run.run(keep_outputs=False)
+    torch.cuda.synchronize()
+    n_launch = args.steps * (len(wl.phases) + cfg.decode_steps)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    rdx.timing_begin(n_launch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run.run(keep_outputs=False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms, kinds = rdx.timing_read(n_launch)
+    assert len(ms) == n_launch, (len(ms), n_launch)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- per-launch kernel durations (ms), reshaped [steps, launches/step] ----
+    per_step = ms.reshape(args.steps, -1)
+    n_ph = len(wl.phases)
+    # launch order per step: extend of phase 0 .. extend of last phase, decode steps after the last extend
+    ext_ms = per_step[:, :n_ph]
+    dec_ms = per_step[:, n_ph:]
+    member_phases = list(range(1, n_ph)) if n_ph > 1 else [0]
+    member_reqs = [r for p in member_phases for r in wl.phases[p].requests]
+    member_tokens = sum(r.own_len for r in member_reqs)
+    ext_member_s = ext_ms[:, member_phases].sum(axis=1).mean() / 1e3
+    ext_flops = extend_flops(cfg, member_reqs)
+    dec_total_s = dec_ms.sum(axis=1).mean() / 1e3 if cfg.decode_steps else 0.0
+    dec_bytes = sum(decode_bytes(wl, t) for t in range(cfg.decode_steps))
+    R = len(wl.leaf_requests)
+    tokens_per_step = sum(run.extend_tokens) + run.decode_tokens
+
+    ext_tflops = ext_flops / ext_member_s / 1e12
+    peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    extend_roof = {"bound": "mfma", "achieved": ext_tflops, "peak": peak_tf, "unit": "TFLOP/s",
+                   "frac": ext_tflops / peak_tf, "traffic": None,
+                   "avg_launch_us": ext_member_s * 1e6 / len(member_phases),
+                   "work_per_step": f"{ext_flops / 1e9:.2f} GFLOP over {member_tokens} member query tokens"}
+    dec_gbs = dec_bytes / dec_total_s / 1e9 if dec_total_s else 0.0
+    decode_roof = {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": dec_gbs / PEAK_HBM_GBS, "traffic": None,
+                   "avg_launch_us": dec_total_s * 1e6 / max(1, cfg.decode_steps),
+                   "work_per_step": f"{dec_bytes / 1e9:.3f} GB over {cfg.decode_steps} launches"}
+    dominant = decode_roof if dec_total_s >= ext_ms.sum(axis=1).mean() / 1e3 else extend_roof
+    dominant = dict(dominant, kernel="decode attention" if dominant is decode_roof else "extend attention")
+
+    line = {
+        "metric": "extend query-tokens/s + decode tokens/s; % MFMA peak / % HBM GB/s, 1 MI355X",
+        "value": tokens_per_step / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1)*sigma Q/K/V, uniform token ids)",
+        "config": {"workload": cfg.name, "levels": [list(l) for l in cfg.levels],
+                   "decode_steps": cfg.decode_steps, "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "tokens_per_step": tokens_per_step, "parallelism": "none (1 GPU)"},
+        "extend_query_tokens_per_s": member_tokens / ext_member_s,
+        "decode_tokens_per_s": cfg.decode_steps * R / dec_total_s if dec_total_s else None,
+        "roofline": dominant,
+        "extend_roofline": extend_roof,
+        "decode_roofline": decode_roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,257 @@
+/*
+ * rdx.h -- C ABI of librdx: prefix-shared attention over a token-granular
+ * paged KV pool whose prefixes are shared through a radix tree.
+ *
+ * Operations and the passages that define them:
+ *   radix tree (match / insert / lock / LRU leaf eviction, page size 1):
+ *     SGLang explainer (0h-n0.github.io ... paper-2312-07104-scheduling),
+ *     RadixAttention section; SGLang paper notes (knowledge.zhaoweiguo.com
+ *     ... 2312.07104_sglang), section 3 and Figure 3.
+ *   matching unit (a match counted in whole units of u tokens):
+ *     vLLM-vs-SGLang prefix caching page (zvxbase.com), worked example and
+ *     matching-unit section.
+ *   prefix-shared attention with horizontal fusion (shared-prefix part and
+ *     distinct part in one launch, partial softmax states combined):
+ *     BatchLLM explainer (0h-n0.github.io ... paper-2412-03594), Horizontal
+ *     Fusion section.
+ *   decode over prefix + distinct pages: same page, prefix-shared attention;
+ *     vLLM-vs-SGLang page, section on prefill vs decode.
+ *
+ * Conventions
+ *   - Every function returns RDX_OK (0) or a negative RDX_E* code; after an
+ *     error rdx_last_error() describes it (thread-local, valid until the next
+ *     rdx call on the thread).  A failed call leaves all state unchanged.
+ *   - Slots (= pages = one token's KV row) are int32 in [0, num_slots).
+ *   - Host pointers are caller-owned; output buffers must hold the stated
+ *     capacity.  Device pointers are caller-owned device memory; the library
+ *     never allocates or frees device memory (it allocates pinned host
+ *     staging memory for plan uploads).
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Device calls only enqueue work; they do not synchronise.  Faults inside
+ *     a kernel surface at the caller's next synchronisation.
+ *   - Not thread-safe per object: one thread drives a tree and its plans.
+ */
+#ifndef RDX_H
+#define RDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RDX_OK 0
+#define RDX_EINVAL (-1)       /* bad argument */
+#define RDX_ENOSPC (-2)       /* free + evictable slots < requested */
+#define RDX_ESTATE (-3)       /* unknown node, refcount underflow, slot not private */
+#define RDX_EUNSUPPORTED (-4) /* dtype / head_dim / head ratio not built */
+#define RDX_EDEVICE (-5)      /* a HIP call failed */
+
+const char* rdx_last_error(void);
+const char* rdx_version(void);
+
+/* ------------------------------------------------------------------ tree */
+typedef struct rdx_tree rdx_tree;
+
+/* A radix tree over token ids whose values are KV slots, page size 1.
+ * num_slots: size of the KV pool (slots 0..num_slots-1 start free).
+ * match_unit: rdx_match_prefix reports matches rounded down to a multiple of
+ * it (1 = token-granular).  Errors: EINVAL (num_slots <= 0 or >= 2^31,
+ * match_unit < 1). */
+int rdx_tree_create(int64_t num_slots, int32_t match_unit, rdx_tree** out);
+void rdx_tree_destroy(rdx_tree* tree);
+
+/* Longest cached prefix of tokens[0..n): *out_len = m (rounded to the match
+ * unit), out_slots[0..m) = its slots (capacity n), *out_node = the node that
+ * ends exactly at m (0 = root when m == 0).  A match ending inside an edge
+ * splits the edge there.  Ticks the LRU clock and stamps every node on the
+ * path (a split keeps the old stamp and id on its lower part; the new upper
+ * part takes the next node id and the reference count).  Errors: EINVAL. */
+int rdx_match_prefix(rdx_tree* tree, const int32_t* tokens, int64_t n,
+                     int32_t* out_slots, int64_t* out_len, int64_t* out_node);
+
+/* +1 / -1 on the reference count of every node from `node` up to the root.
+ * Referenced nodes are never evicted.  Errors: ESTATE (unknown node,
+ * underflow). node 0 (root) is a no-op. */
+int rdx_lock(rdx_tree* tree, int64_t node);
+int rdx_unlock(rdx_tree* tree, int64_t node);
+
+/* The n smallest free slots, ascending, into out_slots (capacity n); they
+ * become private to the caller.  If fewer than n are free, least recently
+ * used unreferenced leaves are evicted (whole nodes, smallest (last access,
+ * node id) first, repeating as parents become leaves) until n are free.
+ * Errors: EINVAL (n < 0), ENOSPC (free + evictable < n; nothing changes). */
+int rdx_alloc(rdx_tree* tree, int64_t n, int32_t* out_slots);
+
+/* Return private slots to the free set.  Errors: EINVAL (out of range),
+ * ESTATE (a slot not private, or listed twice). */
+int rdx_free(rdx_tree* tree, const int32_t* slots, int64_t n);
+
+/* Insert tokens[0..n) with their slots.  *out_present = k, the length already
+ * cached (the tree keeps its own slots for [0,k); the caller frees its
+ * duplicates in [matched, k)); slots[k..n) must be private and become the
+ * tree's.  *out_node = the node ending at n (split if inside an edge).  Ticks
+ * the clock and stamps the path.  Errors: EINVAL, ESTATE. */
+int rdx_insert(rdx_tree* tree, const int32_t* tokens, const int32_t* slots, int64_t n,
+               int64_t* out_present, int64_t* out_node);
+
+/* Evict LRU unreferenced leaves until at least n_tokens were freed or none
+ * is left; *out_freed = tokens freed (may exceed n_tokens). */
+int rdx_evict(rdx_tree* tree, int64_t n_tokens, int64_t* out_freed);
+
+typedef struct rdx_stats {
+  int64_t num_slots;
+  int64_t free;      /* slots in the free set */
+  int64_t cached;    /* slots held by the tree */
+  int64_t evictable; /* tree slots with reference count 0 */
+  int64_t private_;  /* slots allocated to callers and not inserted */
+  int64_t nodes;     /* nodes excluding the root */
+  int64_t evictions; /* nodes evicted so far */
+  int64_t clock;     /* LRU clock (match + insert calls) */
+} rdx_stats;
+int rdx_tree_stats(const rdx_tree* tree, rdx_stats* out);
+
+typedef struct rdx_node_info {
+  int64_t id, parent, start, length, ref, last_access, num_children;
+} rdx_node_info;
+/* Introspection of one node; out_slots (capacity info.length, may be NULL)
+ * receives its slots.  Errors: ESTATE (unknown node). */
+int rdx_node_get(const rdx_tree* tree, int64_t node, rdx_node_info* out, int32_t* out_slots);
+
+/* ------------------------------------------------------------ attention */
+#define RDX_F32 0
+#define RDX_BF16 1
+
+typedef struct rdx_attn_desc {
+  int32_t dtype;        /* RDX_F32 or RDX_BF16: Q, the KV pools and O */
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv, divides Hq; query head h reads KV head h*Hkv/Hq */
+  int32_t head_dim;     /* 64 or 128 */
+  float sm_scale;       /* 0 -> 1/sqrt(head_dim) */
+  int32_t reserved;
+  int64_t num_slots;    /* rows of each KV pool */
+} rdx_attn_desc;
+/* Layouts (row-major, contiguous):
+ *   K pool, V pool   [num_slots][Hkv][head_dim]
+ *   Q, O, new K/V    [tokens][H][head_dim]   (H = Hq for Q/O, Hkv for K/V)
+ *   page table       int32 [rows][ld]: row r, position p -> slot  */
+
+/* Scatter new K/V rows into the pools: pool[slots[i]] = new[i], i < n.
+ * slots: device int32[n], distinct.  Errors: EINVAL, EUNSUPPORTED, EDEVICE. */
+int rdx_kv_store(const rdx_attn_desc* desc, void* k_pool, void* v_pool,
+                 const void* k_new, const void* v_new, const int32_t* slots,
+                 int64_t n, void* stream);
+
+/* ------------------------------------------------------------------ plan */
+typedef struct rdx_plan rdx_plan;
+#define RDX_PLAN_EXTEND 0
+#define RDX_PLAN_DECODE 1
+
+/* One batch of requests.  Request i owns page-table row row[i]; after this
+ * batch its positions 0..kv_len[i]-1 hold KV; its q_len[i] newest positions
+ * kv_len[i]-q_len[i] .. kv_len[i]-1 are the new tokens, which are also its
+ * queries (caller Q rows sum(q_len[0..i)) .. +q_len[i]).  node[i] is the
+ * locked tree node ending the request's cached prefix (its depth must not
+ * exceed kv_len-q_len; 0 = nothing cached); nodes reached by two or more
+ * requests of the batch are attended to once for all of them.  Positions
+ * [0, written[i]) of the row already hold the right slots on the device; the
+ * upload writes [written[i], kv_len[i]) from the tree path and new_slots
+ * (request-major, sum(q_len) entries). */
+typedef struct rdx_batch {
+  int32_t num_reqs;
+  int32_t reserved;
+  const int64_t* node;
+  const int32_t* row;
+  const int32_t* kv_len;
+  const int32_t* q_len;
+  const int32_t* written;
+  const int32_t* new_slots;
+} rdx_batch;
+
+/* kind: RDX_PLAN_EXTEND or RDX_PLAN_DECODE; target_items: the launch size the
+ * planner splits key ranges towards (0 = default).  Errors: EINVAL,
+ * EUNSUPPORTED. */
+int rdx_plan_create(const rdx_attn_desc* desc, int32_t kind, int32_t target_items, rdx_plan** out);
+void rdx_plan_destroy(rdx_plan* plan);
+
+/* Build the work list of one batch: requests are ordered depth-first by
+ * their shared nodes, queries are packed into row tiles, each tile gets the
+ * shared segments and per-request own ranges it must attend to, and long key
+ * ranges are split into separate work items whose partial softmax states are
+ * merged in the same launch.  page_table_ld: row stride of the page table.
+ * Errors: EINVAL (inconsistent batch), ESTATE (unknown node). */
+int rdx_plan_build(rdx_plan* plan, const rdx_tree* tree, const rdx_batch* batch,
+                   int64_t page_table_ld);
+
+typedef struct rdx_plan_info {
+  int64_t device_bytes;      /* size of the device plan buffer */
+  int64_t workspace_bytes;   /* attention workspace (0 when nothing is split) */
+  int64_t new_slots_offset;  /* byte offset of the new-token slot list (int32[num_new]) */
+  int64_t num_new;           /* = sum(q_len) */
+  int64_t num_items, num_tiles, num_jobs, num_split_tiles, num_shared_segments;
+  int64_t key_rows;          /* sum over items of (tile rows x keys): work estimate */
+} rdx_plan_info;
+int rdx_plan_get_info(const rdx_plan* plan, rdx_plan_info* out);
+
+/* Copy the plan to dev_plan (device, >= device_bytes) on `stream` and write
+ * the batch's page-table entries into page_table (device int32
+ * [page_table_rows][ld]).  Reuses the plan's pinned staging buffer once the
+ * previous upload has left it.  Errors: EINVAL, EDEVICE. */
+int rdx_plan_upload(rdx_plan* plan, void* dev_plan, int64_t dev_plan_bytes,
+                    int32_t* page_table, int64_t page_table_rows, void* stream);
+
+/* Host view of a built plan (for tests and tools).  Arrays stay valid until
+ * the next rdx_plan_build.  Record layouts are int32:
+ *   item    [8] tile, kv_head, job_begin, job_end, contrib, 0, 0, 0
+ *   tile    [8] tok_begin, n_tok, n_contrib, contrib_begin, counter (-1 = no merge), 0,0,0
+ *   job     [8] page_row, key_begin, key_end, tok_lo, tok_hi, causal, 0, 0
+ *   token   [2] q_index, position
+ *   contrib [4] tok_lo, tok_hi, ws_token_base, 0 */
+typedef struct rdx_plan_view {
+  const int32_t* items; int64_t num_items;
+  const int32_t* tiles; int64_t num_tiles;
+  const int32_t* jobs; int64_t num_jobs;
+  const int32_t* tokens; int64_t num_tokens;
+  const int32_t* contribs; int64_t num_contribs;
+  int32_t tile_rows;       /* query rows per tile (tokens x Hq/Hkv) */
+  int32_t group;           /* Hq / Hkv */
+} rdx_plan_view;
+int rdx_plan_get_view(const rdx_plan* plan, rdx_plan_view* out);
+
+/* ------------------------------------------------------ attention launch */
+/* Prefix-shared attention of one plan (extend or decode kind respectively):
+ * for every new token at position p and query head h,
+ *   O[tok][h] = softmax_j(scale * q.k_j) v_j  over positions j <= p of its row,
+ * reading K/V through the page table.  One launch: work items cover
+ * (row tile, KV head, key range); tiles whose key ranges were split merge
+ * their partial (o, max, sum) states by log-sum-exp in the same launch (the
+ * last item to finish merges).  q/o: device [sum q_len][Hq][head_dim] in
+ * caller order.  workspace: device, >= workspace_bytes, zero-filled once
+ * before its first use (every launch leaves its counters at zero again);
+ * may be NULL when workspace_bytes == 0.  Launches that share a workspace
+ * must not overlap.  Errors: EINVAL, EUNSUPPORTED, EDEVICE. */
+int rdx_extend_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const void* dev_plan,
+                         const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, void* o, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const void* dev_plan,
+                         const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, void* o, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------- launch timing */
+/* For benchmarks.  rdx_timing_begin(cap) starts recording: the next (up to
+ * cap) attention launches are issued with HIP events bound to the kernel
+ * dispatch itself (hipExtLaunchKernel), so time the GPU spends waiting for
+ * the host between launches is not counted.  rdx_timing_read waits for the
+ * recorded launches, writes their durations in milliseconds and kinds
+ * (RDX_PLAN_EXTEND / RDX_PLAN_DECODE) in launch order (capacity cap), sets
+ * *out_n, and stops recording.  Errors: EINVAL, EDEVICE. */
+int rdx_timing_begin(int32_t cap);
+int rdx_timing_read(float* out_ms, int32_t* out_kind, int32_t cap, int32_t* out_n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RDX_H */

@@ -30,7 +30,8 @@ Readings of points the pages leave open (the product's tree follows the same):
     reference count 0 and no children; whole segments are evicted; evicting
     may free more than asked; parents left childless become candidates;
   * allocation returns the n smallest free slot ids in ascending order and
-    evicts only the shortfall; if free + evictable < n nothing changes;
+    evicts only the shortfall; if free + evictable < n nothing changes
+    (evictable: tokens of segments with no referenced segment at or below);
   * insert keeps the tree's slots for the part already present and reports
     its length; the caller frees its own duplicates;
   * lock/unlock add/subtract 1 on every segment from the node to the root;
@@ -229,7 +230,16 @@ class TokenTrieCache:
             s.ref -= 1
 
     def evictable_tokens(self) -> int:
-        return sum(len(self._chain(s)) for s in self.segs.values() if s.ref == 0)
+        """Tokens of segments with no referenced segment at or below them
+        (only those can ever become unreferenced leaves)."""
+        pinned = set()
+        for s in self.segs.values():
+            if s.ref > 0:
+                p = s
+                while p is not None and p.id not in pinned:
+                    pinned.add(p.id)
+                    p = self._parent_seg(p)
+        return sum(len(self._chain(s)) for s in self.segs.values() if s.id not in pinned)
 
     def alloc(self, n: int):
         if n < 0:

@@ -57,10 +57,14 @@ def request_attention(wl, req):
     return o[: req.own_len], o[req.own_len:]
 
 
-def run_workload(wl, num_slots: int | None = None, attention_for=None, match_unit: int = 1):
-    """attention_for: None = every request, an iterable of rids, or () for none."""
+def run_workload(wl, num_slots: int | None = None, attention_for=None, match_unit: int = 1, prepare=None):
+    """attention_for: None = every request, an iterable of rids, or () for none.
+    prepare: optional callable applied to the fresh cache before the phases
+    (e.g. allocations that fragment the pool)."""
     cfg = wl.cfg
     cache = TokenTrieCache(num_slots or cfg.total_tokens(), match_unit)
+    if prepare is not None:
+        prepare(cache)
     res = OracleResult()
     want = None if attention_for is None else set(attention_for)
     n_phases = len(wl.phases)

@@ -1,0 +1,182 @@
+// C ABI: host-side entry points (tree, planner).  The device entry points
+// live in device.hip.
+#include <cmath>
+#include <new>
+
+#include "common.h"
+#include "plan.h"
+#include "radix_tree.h"
+
+struct rdx_tree {
+  rdx::RadixTree impl;
+  rdx_tree(int64_t n, int32_t u) : impl(n, u) {}
+};
+
+namespace rdx {
+std::string& last_error() {
+  thread_local std::string msg;
+  return msg;
+}
+}  // namespace rdx
+
+using rdx::fail;
+
+extern "C" {
+
+const char* rdx_last_error(void) { return rdx::last_error().c_str(); }
+const char* rdx_version(void) { return "rdx 0.1 gfx950"; }
+
+int rdx_tree_create(int64_t num_slots, int32_t match_unit, rdx_tree** out) {
+  if (!out || num_slots <= 0 || num_slots >= ((int64_t)1 << 31) || match_unit < 1)
+    return fail(RDX_EINVAL, "rdx_tree_create: need 0 < num_slots < 2^31 and match_unit >= 1");
+  try {
+    *out = new rdx_tree(num_slots, match_unit);
+  } catch (const std::bad_alloc&) {
+    return fail(RDX_EINVAL, "rdx_tree_create: out of host memory");
+  }
+  return rdx::ok();
+}
+
+void rdx_tree_destroy(rdx_tree* tree) { delete tree; }
+
+int rdx_match_prefix(rdx_tree* t, const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* out_len,
+                     int64_t* out_node) {
+  if (!t) return fail(RDX_EINVAL, "rdx_match_prefix: null tree");
+  return t->impl.match_prefix(tokens, n, out_slots, out_len, out_node);
+}
+
+int rdx_lock(rdx_tree* t, int64_t node) {
+  if (!t) return fail(RDX_EINVAL, "rdx_lock: null tree");
+  return t->impl.lock(node);
+}
+
+int rdx_unlock(rdx_tree* t, int64_t node) {
+  if (!t) return fail(RDX_EINVAL, "rdx_unlock: null tree");
+  return t->impl.unlock(node);
+}
+
+int rdx_alloc(rdx_tree* t, int64_t n, int32_t* out_slots) {
+  if (!t) return fail(RDX_EINVAL, "rdx_alloc: null tree");
+  return t->impl.alloc(n, out_slots);
+}
+
+int rdx_free(rdx_tree* t, const int32_t* slots, int64_t n) {
+  if (!t) return fail(RDX_EINVAL, "rdx_free: null tree");
+  return t->impl.free_slots(slots, n);
+}
+
+int rdx_insert(rdx_tree* t, const int32_t* tokens, const int32_t* slots, int64_t n, int64_t* out_present,
+               int64_t* out_node) {
+  if (!t) return fail(RDX_EINVAL, "rdx_insert: null tree");
+  return t->impl.insert(tokens, slots, n, out_present, out_node);
+}
+
+int rdx_evict(rdx_tree* t, int64_t n_tokens, int64_t* out_freed) {
+  if (!t) return fail(RDX_EINVAL, "rdx_evict: null tree");
+  return t->impl.evict(n_tokens, out_freed);
+}
+
+int rdx_tree_stats(const rdx_tree* t, rdx_stats* out) {
+  if (!t || !out) return fail(RDX_EINVAL, "rdx_tree_stats: null argument");
+  const auto& x = t->impl;
+  out->num_slots = x.num_slots();
+  out->free = x.num_free();
+  out->cached = x.count_state(rdx::RadixTree::kTree);
+  out->evictable = x.evictable_tokens();
+  out->private_ = x.count_state(rdx::RadixTree::kPrivate);
+  out->nodes = x.num_nodes();
+  out->evictions = x.evictions();
+  out->clock = x.clock();
+  return rdx::ok();
+}
+
+int rdx_node_get(const rdx_tree* t, int64_t node, rdx_node_info* out, int32_t* out_slots) {
+  if (!t || !out) return fail(RDX_EINVAL, "rdx_node_get: null argument");
+  const rdx::Node* n = t->impl.find(node);
+  if (!n) return fail(RDX_ESTATE, "rdx_node_get: unknown node %lld", (long long)node);
+  out->id = n->id;
+  out->parent = (n->parent == nullptr || n->parent == t->impl.root()) ? 0 : n->parent->id;
+  out->start = n->start;
+  out->length = (int64_t)n->key.size();
+  out->ref = n->ref;
+  out->last_access = n->last_access;
+  out->num_children = (int64_t)n->children.size();
+  if (out_slots)
+    for (size_t i = 0; i < n->slots.size(); ++i) out_slots[i] = n->slots[i];
+  return rdx::ok();
+}
+
+int rdx_plan_create(const rdx_attn_desc* desc, int32_t kind, int32_t target_items, rdx_plan** out) {
+  if (!out || !desc) return fail(RDX_EINVAL, "rdx_plan_create: null argument");
+  if (kind != RDX_PLAN_EXTEND && kind != RDX_PLAN_DECODE) return fail(RDX_EINVAL, "rdx_plan_create: bad kind %d", kind);
+  if (target_items < 0) return fail(RDX_EINVAL, "rdx_plan_create: negative target_items");
+  int rc = rdx::check_desc(desc);
+  if (rc) return rc;
+  auto* p = new (std::nothrow) rdx::Plan();
+  if (!p) return fail(RDX_EINVAL, "rdx_plan_create: out of host memory");
+  p->desc = *desc;
+  p->kind = kind;
+  p->target_items = target_items;
+  *out = reinterpret_cast<rdx_plan*>(p);
+  return rdx::ok();
+}
+
+int rdx_plan_build(rdx_plan* plan, const rdx_tree* tree, const rdx_batch* batch, int64_t ld) {
+  if (!plan || !tree || !batch) return fail(RDX_EINVAL, "rdx_plan_build: null argument");
+  auto* p = reinterpret_cast<rdx::Plan*>(plan);
+  p->ld = ld;
+  return p->build(tree->impl, *batch, ld);
+}
+
+int rdx_plan_get_info(const rdx_plan* plan, rdx_plan_info* out) {
+  if (!plan || !out) return fail(RDX_EINVAL, "rdx_plan_get_info: null argument");
+  auto* p = reinterpret_cast<const rdx::Plan*>(plan);
+  if (!p->built) return fail(RDX_ESTATE, "rdx_plan_get_info: plan not built");
+  out->device_bytes = p->total_words * 4;
+  out->workspace_bytes = p->ws_bytes;
+  out->new_slots_offset = p->off_new * 4;
+  out->num_new = (int64_t)p->new_slots.size();
+  out->num_items = (int64_t)p->items.size() / rdx::kItemWords;
+  out->num_tiles = (int64_t)p->tiles.size() / rdx::kTileWords;
+  out->num_jobs = (int64_t)p->jobs.size() / rdx::kJobWords;
+  out->num_split_tiles = p->num_split_tiles;
+  out->num_shared_segments = p->num_shared_segments;
+  out->key_rows = p->key_rows;
+  return rdx::ok();
+}
+
+int rdx_plan_get_view(const rdx_plan* plan, rdx_plan_view* out) {
+  if (!plan || !out) return fail(RDX_EINVAL, "rdx_plan_get_view: null argument");
+  auto* p = reinterpret_cast<const rdx::Plan*>(plan);
+  if (!p->built) return fail(RDX_ESTATE, "rdx_plan_get_view: plan not built");
+  out->items = p->items.data();
+  out->num_items = (int64_t)p->items.size() / rdx::kItemWords;
+  out->tiles = p->tiles.data();
+  out->num_tiles = (int64_t)p->tiles.size() / rdx::kTileWords;
+  out->jobs = p->jobs.data();
+  out->num_jobs = (int64_t)p->jobs.size() / rdx::kJobWords;
+  out->tokens = p->toks.data();
+  out->num_tokens = (int64_t)p->toks.size() / rdx::kTokWords;
+  out->contribs = p->contribs.data();
+  out->num_contribs = (int64_t)p->contribs.size() / rdx::kContribWords;
+  out->tile_rows = rdx::kTileRows;
+  out->group = p->group();
+  return rdx::ok();
+}
+
+}  // extern "C"
+
+namespace rdx {
+int check_desc(const rdx_attn_desc* d) {
+  if (!d) return fail(RDX_EINVAL, "null attention descriptor");
+  if (d->dtype != RDX_F32 && d->dtype != RDX_BF16) return fail(RDX_EUNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads)
+    return fail(RDX_EINVAL, "heads: need Hkv > 0 dividing Hq (got %d/%d)", d->num_q_heads, d->num_kv_heads);
+  int g = d->num_q_heads / d->num_kv_heads;
+  if (g > kTileRows || kTileRows % g) return fail(RDX_EUNSUPPORTED, "Hq/Hkv = %d must divide %d", g, kTileRows);
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(RDX_EUNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
+  if (d->num_slots <= 0 || d->num_slots >= ((int64_t)1 << 31)) return fail(RDX_EINVAL, "num_slots out of range");
+  if (!(d->sm_scale >= 0.f) || std::isinf(d->sm_scale)) return fail(RDX_EINVAL, "sm_scale must be finite and >= 0");
+  return ok();
+}
+}  // namespace rdx

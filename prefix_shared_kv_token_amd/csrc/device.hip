@@ -1,0 +1,663 @@
+// Device entry points of librdx for gfx950 (CDNA4): KV scatter, plan upload
+// (page-table writes) and the prefix-shared attention launches.
+//
+// Attention follows the BatchLLM explainer, Horizontal Fusion section: the
+// common-prefix part and each request's own part of prefix-shared attention
+// run as different workgroups of one kernel, and their partial results are
+// combined in that launch.  The partial softmax states (o, running max m,
+// running sum l) are combined with the log-sum-exp rule
+//   M = max_c m_c,  w_c = l_c 2^(m_c - M),  o = sum_c w_c o_c / sum_c w_c
+// (scores kept in the base-2 domain: t = s * scale * log2 e).
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "plan.h"
+
+namespace rdx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;  // 4 waves of 64; wave w owns tile rows [32w, 32w+32)
+
+struct AttnArgs {
+  const int32_t* items;
+  const int32_t* tiles;
+  const int32_t* jobs;
+  const int32_t* toks;
+  const int32_t* contribs;
+  const int32_t* page_table;
+  int64_t ld;
+  const void* q;
+  const void* kp;
+  const void* vp;
+  void* o;
+  int32_t* counters;
+  float* ws_o;
+  float* ws_ml;
+  int64_t ws_tokens;
+  int hq, hkv, group;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(__bf16* p, float v) { *p = (__bf16)v; }
+
+// ---------------------------------------------------------------------------
+// Partial-state epilogue shared by both kernels.
+//
+// A contribution's partial for (tile token t, grouped head hh) lives at
+//   ws_o [((kvh * ws_tokens + base + t - lo) * group + hh) * D + d]
+//   ws_ml[((kvh * ws_tokens + base + t - lo) * group + hh) * 2 + {0:m, 1:l}]
+// with o already normalised by its own l.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__device__ void merge_tile(const AttnArgs& a, const int32_t* tile, int kvh) {
+  const int n_tok = tile[1], n_contrib = tile[2], cbeg = tile[3];
+  const int group = a.group;
+  const int n_rows = n_tok * group;
+  const int64_t hq = a.hq;
+  T* out = reinterpret_cast<T*>(a.o);
+  constexpr int kVec = 4;
+  constexpr int kPer = D / kVec;  // float4 columns per row
+  for (int idx = threadIdx.x; idx < n_rows * kPer; idx += kThreads) {
+    const int row = idx / kPer, col = (idx % kPer) * kVec;
+    const int t = row / group, hh = row % group;
+    float mmax = -INFINITY;
+    for (int c = 0; c < n_contrib; ++c) {
+      const int32_t* cr = a.contribs + (int64_t)(cbeg + c) * kContribWords;
+      if (t < cr[0] || t >= cr[1]) continue;
+      int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
+      mmax = fmaxf(mmax, a.ws_ml[w * 2]);
+    }
+    float acc[kVec] = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int c = 0; c < n_contrib; ++c) {
+      const int32_t* cr = a.contribs + (int64_t)(cbeg + c) * kContribWords;
+      if (t < cr[0] || t >= cr[1]) continue;
+      int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
+      float l = a.ws_ml[w * 2 + 1];
+      if (l <= 0.f) continue;
+      float wt = l * exp2_fast(a.ws_ml[w * 2] - mmax);
+      float4 v = *reinterpret_cast<const float4*>(a.ws_o + w * D + col);
+      acc[0] += wt * v.x;
+      acc[1] += wt * v.y;
+      acc[2] += wt * v.z;
+      acc[3] += wt * v.w;
+      wsum += wt;
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int32_t q_index = a.toks[(int64_t)(tile[0] + t) * kTokWords];
+    T* dst = out + ((int64_t)q_index * hq + (int64_t)kvh * group + hh) * D + col;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) store_out(dst + e, acc[e] * inv);
+  }
+}
+
+// Called by every thread after its partial rows are stored; the last of the
+// tile's contributions to arrive merges them all and resets the counter.
+template <typename T, int D>
+__device__ void arrive_and_merge(const AttnArgs& a, const int32_t* tile, int kvh, int* s_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t* ctr = a.counters + (int64_t)tile[4] * a.hkv + kvh;
+    int prev = atomicAdd(ctr, 1);
+    int last = prev == tile[2] - 1;
+    if (last) *ctr = 0;  // every contribution has arrived: ready for the next launch
+    *s_flag = last;
+  }
+  __syncthreads();
+  if (*s_flag) {
+    __threadfence();
+    merge_tile<T, D>(a, tile, kvh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel.  One workgroup per work item (tile, KV head, key ranges).
+// Wave w holds query rows 32w..32w+31 of the tile; lane (i = lane % 32,
+// h = lane / 32).  Scores are computed transposed, S^T = K Q^T, with the
+// 32x32x16 bf16 MFMA so that each lane owns one query column: the row max is
+// a reduction over the lane's registers plus one exchange with lane ^ 32, and
+// the probabilities feed the P.V MFMA (O^T = V^T P^T) straight from
+// registers.  The contraction order inside a 16-key step is permuted
+// identically on both operands: lane half h holds keys {4h..4h+3, 8+4h..
+// 8+4h+3}; V^T is stored in LDS with its key quads in that order.
+// ---------------------------------------------------------------------------
+template <int D>
+struct SmemBF16 {
+  static constexpr int KS = D + 8;   // K tile row stride (elements), padded
+  static constexpr int VS = 64 + 8;  // V^T tile row stride
+  __bf16 k[64 * KS];
+  __bf16 vt[D * VS];
+  int32_t slot[64];
+  int flag;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+  __shared__ SmemBF16<D> sm;
+  constexpr int KS = SmemBF16<D>::KS, VS = SmemBF16<D>::VS;
+  constexpr int KSTEPS = D / 16;  // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;      // 32-wide d blocks of the output
+
+  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
+  const int kvh = item[1];
+  const int tok_begin = tile[0], n_tok = tile[1];
+  const int group = a.group;
+  const int n_rows = n_tok * group;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int row = wave * 32 + li;  // this lane's query row in the tile
+  const bool row_ok = row < n_rows;
+  const int tloc = row / group;    // tile-local token
+  const bool wave_live = wave * 32 < n_rows;
+
+  // ---- Q (B operand): Q[row][16 ks + 8 h .. +8) ----
+  bf16x8 qreg[KSTEPS];
+  int qpos = 0;
+  {
+    const __bf16* q = reinterpret_cast<const __bf16*>(a.q);
+    if (row_ok) {
+      const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
+      qpos = tk[1];
+      const __bf16* src = q + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qreg[s] = bf16x8{};
+    }
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  const __bf16* kpool = reinterpret_cast<const __bf16*>(a.kp);
+  const __bf16* vpool = reinterpret_cast<const __bf16*>(a.vp);
+  constexpr int CH = D / 8;        // 16-byte chunks per K/V row
+  constexpr int UNITS = 16 * CH;   // (key quad, chunk) units per matrix
+
+  for (int j = item[2]; j < item[3]; ++j) {
+    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+    const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
+    const int k0 = job[1], k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+    // keys visible to this lane: positions < lim
+    int lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+    const bool wave_job = wave_live && __ballot(lim > k0) != 0;
+    for (int kb = k0; kb < k1; kb += 64) {
+      if (threadIdx.x < 64) {
+        int p = kb + threadIdx.x;
+        sm.slot[threadIdx.x] = p < k1 ? prow[p] : -1;
+      }
+      __syncthreads();
+      for (int u = threadIdx.x; u < 2 * UNITS; u += kThreads) {
+        const int which = u / UNITS, uu = u % UNITS, qd = uu / CH, c = uu % CH;
+        const __bf16* base = which ? vpool : kpool;
+        uint4 rows[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int s = sm.slot[4 * qd + r];
+          rows[r] = s >= 0 ? *reinterpret_cast<const uint4*>(base + ((int64_t)s * a.hkv + kvh) * D + 8 * c)
+                           : make_uint4(0, 0, 0, 0);
+        }
+        if (which == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&sm.k[(4 * qd + r) * KS + 8 * c]) = rows[r];
+        } else {
+          const int qk = qd & 3;
+          const int col = 16 * (qd >> 2) + 4 * (qk == 1 ? 2 : (qk == 2 ? 1 : qk));
+          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&rows[0]);
+          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&rows[1]);
+          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&rows[2]);
+          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&rows[3]);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            uint2 lo2 = make_uint2((w0[p] & 0xffffu) | (w1[p] << 16), (w2[p] & 0xffffu) | (w3[p] << 16));
+            uint2 hi2 = make_uint2((w0[p] >> 16) | (w1[p] & 0xffff0000u), (w2[p] >> 16) | (w3[p] & 0xffff0000u));
+            *reinterpret_cast<uint2*>(&sm.vt[(8 * c + 2 * p) * VS + col]) = lo2;
+            *reinterpret_cast<uint2*>(&sm.vt[(8 * c + 2 * p + 1) * VS + col]) = hi2;
+          }
+        }
+      }
+      __syncthreads();
+
+      if (wave_job) {
+        // ---- S^T = K Q^T for 64 keys x this wave's 32 queries ----
+        f32x16 s[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          s[b] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+            bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.k[(32 * b + li) * KS + 16 * ks + 8 * hi]);
+            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[b], 0, 0, 0);
+          }
+        }
+        // ---- mask + online softmax (base 2) ----
+        const int rel = lim - kb;  // keys with local index < rel are visible
+        float mx = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int kl = 32 * b + 8 * (r >> 2) + 4 * hi + (r & 3);
+            float v = kl < rel ? s[b][r] : -INFINITY;
+            s[b][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * c2);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2_fast(m_run - m_use);
+        float lsum = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float p = exp2_fast(fmaf(s[b][r], c2, -m_use));
+            s[b][r] = p;
+            lsum += p;
+          }
+        l_run = l_run * alpha + lsum;
+        m_run = m_new;
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+          for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+        }
+        // ---- P (B operand): 16-key step ks uses registers 8t..8t+7 of block ks/2 ----
+        bf16x8 pk[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 va = *reinterpret_cast<const bf16x8*>(&sm.vt[(32 * b + li) * VS + 16 * ks + 8 * hi]);
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], acc[b], 0, 0, 0);
+          }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (tile[4] < 0) {
+    if (row_ok) {
+      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
+      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * b + 8 * g4 + 4 * hi;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[b][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(dst + d) = v;
+        }
+    }
+    return;
+  }
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+    float* dst = a.ws_o + w * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * b + 8 * g4 + 4 * hi;
+        *reinterpret_cast<float4*>(dst + d) =
+            make_float4(acc[b][4 * g4] * inv, acc[b][4 * g4 + 1] * inv, acc[b][4 * g4 + 2] * inv, acc[b][4 * g4 + 3] * inv);
+      }
+    if (hi == 0) {
+      a.ws_ml[w * 2] = m_run;
+      a.ws_ml[w * 2 + 1] = l_tot;
+    }
+  }
+  arrive_and_merge<__bf16, D>(a, tile, kvh, &sm.flag);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (plain VALU, parity-grade).  One thread per query row of the
+// tile, scalar online softmax over the row's visible keys.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
+  __shared__ int s_flag;
+  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
+  const int kvh = item[1];
+  const int group = a.group;
+  const int n_rows = tile[1] * group;
+  const int row = threadIdx.x;
+  const bool row_ok = row < n_rows;
+  const int tloc = row_ok ? row / group : 0;
+  float q[D], acc[D];
+  float m_run = -INFINITY, l_run = 0.f;
+  int qpos = 0;
+  if (row_ok) {
+    const int32_t* tk = a.toks + (int64_t)(tile[0] + tloc) * kTokWords;
+    qpos = tk[1];
+    const float* src = reinterpret_cast<const float*>(a.q) + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D;
+    for (int d = 0; d < D; ++d) {
+      q[d] = src[d];
+      acc[d] = 0.f;
+    }
+    const float* kpool = reinterpret_cast<const float*>(a.kp);
+    const float* vpool = reinterpret_cast<const float*>(a.vp);
+    for (int j = item[2]; j < item[3]; ++j) {
+      const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+      if (tloc < job[3] || tloc >= job[4]) continue;
+      const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
+      const int end = job[5] ? min(job[2], qpos + 1) : job[2];
+      for (int p = job[1]; p < end; ++p) {
+        const int64_t off = ((int64_t)prow[p] * a.hkv + kvh) * D;
+        float s = 0.f;
+        for (int d = 0; d < D; ++d) s = fmaf(q[d], kpool[off + d], s);
+        const float t = s * a.scale_log2;
+        const float m_new = fmaxf(m_run, t);
+        const float alpha = exp2f(m_run - m_new);
+        const float pw = exp2f(t - m_new);
+        l_run = l_run * alpha + pw;
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(pw, vpool[off + d], acc[d] * alpha);
+        m_run = m_new;
+      }
+    }
+  }
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (tile[4] < 0) {
+    if (row_ok) {
+      const int32_t q_index = a.toks[(int64_t)(tile[0] + tloc) * kTokWords];
+      float* dst = reinterpret_cast<float*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
+      for (int d = 0; d < D; ++d) dst[d] = acc[d] * inv;
+    }
+    return;
+  }
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+    for (int d = 0; d < D; ++d) a.ws_o[w * D + d] = acc[d] * inv;
+    a.ws_ml[w * 2] = m_run;
+    a.ws_ml[w * 2 + 1] = l_run;
+  }
+  arrive_and_merge<float, D>(a, tile, kvh, &s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// KV scatter and page-table writes
+// ---------------------------------------------------------------------------
+__global__ void kv_store_kernel(uint4* __restrict__ kp, uint4* __restrict__ vp, const uint4* __restrict__ kn,
+                                const uint4* __restrict__ vn, const int32_t* __restrict__ slots, int64_t n,
+                                int64_t row_vecs) {
+  const int64_t total = n * row_vecs;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tok = i / row_vecs, e = i % row_vecs;
+    const int64_t dst = (int64_t)slots[tok] * row_vecs + e;
+    kp[dst] = kn[i];
+    vp[dst] = vn[i];
+  }
+}
+
+__global__ void page_table_write_kernel(int32_t* __restrict__ pt, int64_t ld, const int32_t* __restrict__ runs,
+                                        const int32_t* __restrict__ run_slots) {
+  const int32_t* r = runs + (int64_t)blockIdx.x * kRunWords;
+  int32_t* dst = pt + (int64_t)r[0] * ld + r[1];
+  const int32_t* src = run_slots + r[3];
+  for (int i = threadIdx.x; i < r[2]; i += blockDim.x) dst[i] = src[i];
+}
+
+}  // namespace rdx
+
+using namespace rdx;
+
+namespace {
+
+// Launch timing state (see rdx_timing_begin): event pairs reused across runs.
+struct Timing {
+  bool on = false;
+  int32_t cap = 0;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int32_t> kind;
+  int32_t used = 0;
+} g_timing;
+
+template <typename K>
+hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t st, int32_t kind, const AttnArgs& a) {
+  if (g_timing.on && g_timing.used < g_timing.cap) {
+    int32_t i = g_timing.used;
+    while ((int32_t)g_timing.start.size() <= i) {
+      hipEvent_t e0, e1;
+      hipError_t e = hipEventCreate(&e0);
+      if (e != hipSuccess) return e;
+      e = hipEventCreate(&e1);
+      if (e != hipSuccess) return e;
+      g_timing.start.push_back(e0);
+      g_timing.stop.push_back(e1);
+      g_timing.kind.push_back(0);
+    }
+    g_timing.kind[i] = kind;
+    g_timing.used++;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_timing.start[i], g_timing.stop[i], 0, a);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(RDX_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool same_shape(const rdx_attn_desc& a, const rdx_attn_desc& b) {
+  return a.dtype == b.dtype && a.num_q_heads == b.num_q_heads && a.num_kv_heads == b.num_kv_heads &&
+         a.head_dim == b.head_dim && a.num_slots == b.num_slots;
+}
+
+int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t kind, const void* dev_plan,
+                     const void* q, const void* kp, const void* vp, const int32_t* pt, void* o, void* ws,
+                     int64_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!hplan) return fail(RDX_EINVAL, "attention: null plan");
+  const Plan* p = reinterpret_cast<const Plan*>(hplan);
+  if (!p->built) return fail(RDX_ESTATE, "attention: plan not built");
+  if (p->kind != kind) return fail(RDX_EINVAL, "attention: plan kind %d does not match this entry point", p->kind);
+  if (!same_shape(*desc, p->desc)) return fail(RDX_EINVAL, "attention: descriptor differs from the plan's");
+  const int64_t n_items = (int64_t)p->items.size() / kItemWords;
+  if (n_items == 0) return ok();
+  if (!dev_plan || !q || !kp || !vp || !pt || !o) return fail(RDX_EINVAL, "attention: null device pointer");
+  if (p->ws_bytes > 0 && (!ws || ws_bytes < p->ws_bytes))
+    return fail(RDX_EINVAL, "attention: workspace of %lld bytes needed", (long long)p->ws_bytes);
+  if (n_items > INT32_MAX) return fail(RDX_EINVAL, "attention: too many work items");
+  const int32_t* base = reinterpret_cast<const int32_t*>(dev_plan);
+  AttnArgs a;
+  a.items = base + p->off_items;
+  a.tiles = base + p->off_tiles;
+  a.jobs = base + p->off_jobs;
+  a.toks = base + p->off_toks;
+  a.contribs = base + p->off_contribs;
+  a.page_table = pt;
+  a.ld = p->ld;
+  a.q = q;
+  a.kp = kp;
+  a.vp = vp;
+  a.o = o;
+  char* wsb = reinterpret_cast<char*>(ws);
+  a.counters = reinterpret_cast<int32_t*>(wsb);
+  a.ws_o = wsb ? reinterpret_cast<float*>(wsb + p->ws_o_offset) : nullptr;
+  a.ws_ml = wsb ? reinterpret_cast<float*>(wsb + p->ws_ml_offset) : nullptr;
+  a.ws_tokens = p->ws_tokens;
+  a.hq = desc->num_q_heads;
+  a.hkv = desc->num_kv_heads;
+  a.group = a.hq / a.hkv;
+  const float scale = desc->sm_scale > 0.f ? desc->sm_scale : 1.f / sqrtf((float)desc->head_dim);
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid((unsigned)n_items), block(kThreads);
+  hipError_t e;
+  if (desc->dtype == RDX_BF16)
+    e = desc->head_dim == 128 ? launch(attn_bf16_kernel<128>, grid, block, st, kind, a)
+                              : launch(attn_bf16_kernel<64>, grid, block, st, kind, a);
+  else
+    e = desc->head_dim == 128 ? launch(attn_f32_kernel<128>, grid, block, st, kind, a)
+                              : launch(attn_f32_kernel<64>, grid, block, st, kind, a);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int rdx_kv_store(const rdx_attn_desc* desc, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                 const int32_t* slots, int64_t n, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (n < 0) return fail(RDX_EINVAL, "rdx_kv_store: negative n");
+  if (n == 0) return ok();
+  if (!k_pool || !v_pool || !k_new || !v_new || !slots) return fail(RDX_EINVAL, "rdx_kv_store: null pointer");
+  const int64_t esize = desc->dtype == RDX_BF16 ? 2 : 4;
+  const int64_t row_bytes = (int64_t)desc->num_kv_heads * desc->head_dim * esize;
+  if (row_bytes % 16) return fail(RDX_EUNSUPPORTED, "rdx_kv_store: row of %lld bytes", (long long)row_bytes);
+  const int64_t row_vecs = row_bytes / 16;
+  const int64_t total = n * row_vecs;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(kv_store_kernel, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<uint4*>(k_pool), reinterpret_cast<uint4*>(v_pool),
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new), slots, n, row_vecs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "rdx_kv_store launch");
+  return ok();
+}
+
+int rdx_plan_upload(rdx_plan* hplan, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_table,
+                    int64_t page_table_rows, void* stream) {
+  if (!hplan || !dev_plan) return fail(RDX_EINVAL, "rdx_plan_upload: null argument");
+  Plan* p = reinterpret_cast<Plan*>(hplan);
+  if (!p->built) return fail(RDX_ESTATE, "rdx_plan_upload: plan not built");
+  const int64_t bytes = p->total_words * 4;
+  if (dev_plan_bytes < bytes) return fail(RDX_EINVAL, "rdx_plan_upload: device buffer of %lld bytes needed", (long long)bytes);
+  const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
+  if (n_runs > 0 && (!page_table || page_table_rows <= p->max_page_row))
+    return fail(RDX_EINVAL, "rdx_plan_upload: page table with more than %lld rows needed", (long long)p->max_page_row);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!p->event) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    p->event = ev;
+  }
+  if (p->upload_pending) {
+    e = hipEventSynchronize(reinterpret_cast<hipEvent_t>(p->event));
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    p->upload_pending = false;
+  }
+  if (p->pinned_bytes < bytes) {
+    if (p->pinned) hipHostFree(p->pinned);
+    p->pinned = nullptr;
+    p->pinned_bytes = 0;
+    int64_t want = bytes + bytes / 2 + 4096;
+    e = hipHostMalloc(&p->pinned, want, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+    p->pinned_bytes = want;
+  }
+  int32_t* h = reinterpret_cast<int32_t*>(p->pinned);
+  auto put = [&](int64_t off, const std::vector<int32_t>& v) {
+    if (!v.empty()) memcpy(h + off, v.data(), v.size() * 4);
+  };
+  put(p->off_items, p->items);
+  put(p->off_tiles, p->tiles);
+  put(p->off_jobs, p->jobs);
+  put(p->off_toks, p->toks);
+  put(p->off_contribs, p->contribs);
+  put(p->off_runs, p->runs);
+  put(p->off_run_slots, p->run_slots);
+  put(p->off_new, p->new_slots);
+  e = hipMemcpyAsync(dev_plan, p->pinned, bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
+  if (n_runs > 0) {
+    const int32_t* db = reinterpret_cast<const int32_t*>(dev_plan);
+    hipLaunchKernelGGL(page_table_write_kernel, dim3((unsigned)n_runs), dim3(256), 0, st, page_table, p->ld,
+                       db + p->off_runs, db + p->off_run_slots);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "page-table write launch");
+  }
+  e = hipEventRecord(reinterpret_cast<hipEvent_t>(p->event), st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  p->upload_pending = true;
+  return ok();
+}
+
+void rdx_plan_destroy(rdx_plan* hplan) {
+  if (!hplan) return;
+  Plan* p = reinterpret_cast<Plan*>(hplan);
+  if (p->upload_pending && p->event) hipEventSynchronize(reinterpret_cast<hipEvent_t>(p->event));
+  if (p->event) hipEventDestroy(reinterpret_cast<hipEvent_t>(p->event));
+  if (p->pinned) hipHostFree(p->pinned);
+  delete p;
+}
+
+int rdx_extend_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const void* dev_plan, const void* q,
+                         const void* k_pool, const void* v_pool, const int32_t* page_table, void* o, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  return launch_attention(desc, plan, RDX_PLAN_EXTEND, dev_plan, q, k_pool, v_pool, page_table, o, workspace,
+                          workspace_bytes, stream);
+}
+
+int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const void* dev_plan, const void* q,
+                         const void* k_pool, const void* v_pool, const int32_t* page_table, void* o, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  return launch_attention(desc, plan, RDX_PLAN_DECODE, dev_plan, q, k_pool, v_pool, page_table, o, workspace,
+                          workspace_bytes, stream);
+}
+
+int rdx_timing_begin(int32_t cap) {
+  if (cap < 0) return fail(RDX_EINVAL, "rdx_timing_begin: negative capacity");
+  g_timing.on = true;
+  g_timing.cap = cap;
+  g_timing.used = 0;
+  return ok();
+}
+
+int rdx_timing_read(float* out_ms, int32_t* out_kind, int32_t cap, int32_t* out_n) {
+  if (!out_n || cap < 0 || (cap > 0 && (!out_ms || !out_kind))) return fail(RDX_EINVAL, "rdx_timing_read: bad arguments");
+  const int32_t n = g_timing.used < cap ? g_timing.used : cap;
+  for (int32_t i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(g_timing.stop[i]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    e = hipEventElapsedTime(&out_ms[i], g_timing.start[i], g_timing.stop[i]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    out_kind[i] = g_timing.kind[i];
+  }
+  *out_n = n;
+  g_timing.on = false;
+  g_timing.used = 0;
+  return ok();
+}
+
+}  // extern "C"

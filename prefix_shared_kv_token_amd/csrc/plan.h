@@ -1,0 +1,56 @@
+// Batch planner: turns a batch of requests (their locked tree nodes and page
+// table rows) into the work list of one prefix-shared attention launch.
+//
+// Follows the BatchLLM explainer, Horizontal Fusion section: a request
+// attends to the common-prefix KV and to its own KV; the two parts are
+// computed by different workgroups of ONE kernel with tiles sized per part,
+// and their partial results are combined.  Here a part is a "job": a key
+// range of one page-table row, visible to a token range of a row tile.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "rdx.h"
+#include "radix_tree.h"
+
+namespace rdx {
+
+constexpr int kTileRows = 128;   // query rows (token x grouped head) per tile
+constexpr int kKeyBlock = 64;    // keys per inner iteration of the kernels
+
+// Record layouts (int32 words) -- shared with the device code.
+constexpr int kItemWords = 8;     // tile, kv_head, job_begin, job_end, contrib
+constexpr int kTileWords = 8;     // tok_begin, n_tok, n_contrib, contrib_begin, counter
+constexpr int kJobWords = 8;      // page_row, key_begin, key_end, tok_lo, tok_hi, causal
+constexpr int kTokWords = 2;      // q_index, position
+constexpr int kContribWords = 4;  // tok_lo, tok_hi, ws_token_base
+constexpr int kRunWords = 4;      // page_row, pos_begin, count, src_offset
+
+struct Plan {
+  rdx_attn_desc desc{};
+  int32_t kind = 0;
+  int32_t target_items = 0;
+  int64_t ld = 0;
+  // host records
+  std::vector<int32_t> items, tiles, jobs, toks, contribs, runs, run_slots, new_slots;
+  int64_t num_split_tiles = 0, num_shared_segments = 0, ws_tokens = 0, key_rows = 0;
+  int64_t max_page_row = -1;
+  // device blob layout, in int32 words
+  int64_t off_items = 0, off_tiles = 0, off_jobs = 0, off_toks = 0, off_contribs = 0,
+          off_runs = 0, off_run_slots = 0, off_new = 0, total_words = 0;
+  int64_t ws_counter_bytes = 0, ws_o_offset = 0, ws_ml_offset = 0, ws_bytes = 0;
+  bool built = false;
+  // upload staging (pinned host memory + completion event), owned by the plan
+  void* pinned = nullptr;
+  int64_t pinned_bytes = 0;
+  void* event = nullptr;
+  bool upload_pending = false;
+
+  int group() const { return desc.num_q_heads / desc.num_kv_heads; }
+  int tile_tokens() const { return kTileRows / group(); }
+  int build(const RadixTree& tree, const rdx_batch& b, int64_t ld);
+  void layout();
+};
+
+}  // namespace rdx

@@ -1,0 +1,304 @@
+"""ctypes binding of librdx (argument marshalling only).
+
+Every function here forwards to the C ABI declared in include/rdx.h; the
+computation happens in the library (host tree and planner in C++, device
+work in HIP kernels).  Device arguments are torch tensors (only their data
+pointers cross the boundary) or raw integer addresses; `stream` defaults to
+torch's current stream.  If librdx.so is missing this module raises: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librdx.so")
+
+OK, EINVAL, ENOSPC, ESTATE, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+PLAN_EXTEND, PLAN_DECODE = 0, 1
+
+i32p = ctypes.POINTER(ctypes.c_int32)
+i64p = ctypes.POINTER(ctypes.c_int64)
+vp = ctypes.c_void_p
+i64 = ctypes.c_int64
+i32 = ctypes.c_int32
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [(n, i64) for n in ("num_slots", "free", "cached", "evictable", "private",
+                                   "nodes", "evictions", "clock")]
+
+
+class NodeInfo(ctypes.Structure):
+    _fields_ = [(n, i64) for n in ("id", "parent", "start", "length", "ref", "last_access", "num_children")]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("dtype", i32), ("num_q_heads", i32), ("num_kv_heads", i32), ("head_dim", i32),
+                ("sm_scale", ctypes.c_float), ("reserved", i32), ("num_slots", i64)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("num_reqs", i32), ("reserved", i32), ("node", i64p), ("row", i32p), ("kv_len", i32p),
+                ("q_len", i32p), ("written", i32p), ("new_slots", i32p)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, i64) for n in ("device_bytes", "workspace_bytes", "new_slots_offset", "num_new",
+                                   "num_items", "num_tiles", "num_jobs", "num_split_tiles",
+                                   "num_shared_segments", "key_rows")]
+
+
+class PlanView(ctypes.Structure):
+    _fields_ = [("items", i32p), ("num_items", i64), ("tiles", i32p), ("num_tiles", i64),
+                ("jobs", i32p), ("num_jobs", i64), ("tokens", i32p), ("num_tokens", i64),
+                ("contribs", i32p), ("num_contribs", i64), ("tile_rows", i32), ("group", i32)]
+
+
+_SIGS = {
+    "rdx_last_error": (ctypes.c_char_p, []),
+    "rdx_version": (ctypes.c_char_p, []),
+    "rdx_tree_create": (ctypes.c_int, [i64, i32, ctypes.POINTER(vp)]),
+    "rdx_tree_destroy": (None, [vp]),
+    "rdx_match_prefix": (ctypes.c_int, [vp, i32p, i64, i32p, i64p, i64p]),
+    "rdx_lock": (ctypes.c_int, [vp, i64]),
+    "rdx_unlock": (ctypes.c_int, [vp, i64]),
+    "rdx_alloc": (ctypes.c_int, [vp, i64, i32p]),
+    "rdx_free": (ctypes.c_int, [vp, i32p, i64]),
+    "rdx_insert": (ctypes.c_int, [vp, i32p, i32p, i64, i64p, i64p]),
+    "rdx_evict": (ctypes.c_int, [vp, i64, i64p]),
+    "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
+    "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
+    "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),
+    "rdx_plan_create": (ctypes.c_int, [ctypes.POINTER(AttnDesc), i32, i32, ctypes.POINTER(vp)]),
+    "rdx_plan_destroy": (None, [vp]),
+    "rdx_plan_build": (ctypes.c_int, [vp, vp, ctypes.POINTER(Batch), i64]),
+    "rdx_plan_get_info": (ctypes.c_int, [vp, ctypes.POINTER(PlanInfo)]),
+    "rdx_plan_get_view": (ctypes.c_int, [vp, ctypes.POINTER(PlanView)]),
+    "rdx_plan_upload": (ctypes.c_int, [vp, vp, i64, vp, i64, vp]),
+    "rdx_extend_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+    "rdx_decode_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+    "rdx_timing_begin": (ctypes.c_int, [i32]),
+    "rdx_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), i32p, i32, i32p]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+class RdxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"rdx error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise RdxError(rc, lib().rdx_last_error().decode())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _p32(a: np.ndarray):
+    return a.ctypes.data_as(i32p)
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# --------------------------------------------------------------------- tree
+class Tree:
+    """rdx_tree: radix tree + slot allocator (host)."""
+
+    def __init__(self, num_slots: int, match_unit: int = 1):
+        h = vp()
+        _check(lib().rdx_tree_create(num_slots, match_unit, ctypes.byref(h)))
+        self._h = h
+        self.num_slots = num_slots
+        self._buf = np.empty(0, np.int32)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.rdx_tree_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def match_prefix(self, tokens):
+        t = _i32(tokens)
+        out = np.empty(max(1, len(t)), np.int32)
+        m, node = i64(), i64()
+        _check(lib().rdx_match_prefix(self._h, _p32(t), len(t), _p32(out), ctypes.byref(m), ctypes.byref(node)))
+        return m.value, out[: m.value], node.value
+
+    def lock(self, node: int):
+        _check(lib().rdx_lock(self._h, node))
+
+    def unlock(self, node: int):
+        _check(lib().rdx_unlock(self._h, node))
+
+    def alloc(self, n: int, out: np.ndarray | None = None) -> np.ndarray:
+        if out is None:
+            out = np.empty(max(1, n), np.int32)
+        _check(lib().rdx_alloc(self._h, n, _p32(out)))
+        return out[:n]
+
+    def free(self, slots):
+        s = _i32(slots)
+        _check(lib().rdx_free(self._h, _p32(s), len(s)))
+
+    def insert(self, tokens, slots):
+        t, s = _i32(tokens), _i32(slots)
+        if len(t) != len(s):
+            raise ValueError("tokens and slots differ in length")
+        k, node = i64(), i64()
+        _check(lib().rdx_insert(self._h, _p32(t), _p32(s), len(t), ctypes.byref(k), ctypes.byref(node)))
+        return k.value, node.value
+
+    def evict(self, n_tokens: int) -> int:
+        f = i64()
+        _check(lib().rdx_evict(self._h, n_tokens, ctypes.byref(f)))
+        return f.value
+
+    def stats(self) -> dict:
+        s = Stats()
+        _check(lib().rdx_tree_stats(self._h, ctypes.byref(s)))
+        return {n: getattr(s, n) for n, _ in Stats._fields_}
+
+    def node(self, node_id: int) -> dict:
+        info = NodeInfo()
+        _check(lib().rdx_node_get(self._h, node_id, ctypes.byref(info), None))
+        slots = np.empty(max(1, info.length), np.int32)
+        _check(lib().rdx_node_get(self._h, node_id, ctypes.byref(info), _p32(slots)))
+        d = {n: getattr(info, n) for n, _ in NodeInfo._fields_}
+        d["slots"] = slots[: info.length].copy()
+        return d
+
+
+# --------------------------------------------------------------------- plan
+def attn_desc(dtype: int, num_q_heads: int, num_kv_heads: int, head_dim: int, num_slots: int,
+              sm_scale: float = 0.0) -> AttnDesc:
+    return AttnDesc(dtype, num_q_heads, num_kv_heads, head_dim, sm_scale, 0, num_slots)
+
+
+class Plan:
+    """rdx_plan: work list of one extend or decode launch."""
+
+    def __init__(self, desc: AttnDesc, kind: int, target_items: int = 0):
+        h = vp()
+        _check(lib().rdx_plan_create(ctypes.byref(desc), kind, target_items, ctypes.byref(h)))
+        self._h = h
+        self.desc = desc
+        self.kind = kind
+        self.target = target_items
+        self._keep = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.rdx_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def build(self, tree: Tree, node, row, kv_len, q_len, written, new_slots, page_table_ld: int):
+        node = np.ascontiguousarray(node, np.int64)
+        arrs = [_i32(row), _i32(kv_len), _i32(q_len), _i32(written), _i32(new_slots)]
+        b = Batch(len(node), 0, node.ctypes.data_as(i64p), *[_p32(a) for a in arrs])
+        self._keep = (node, arrs)
+        _check(lib().rdx_plan_build(self._h, tree.handle, ctypes.byref(b), page_table_ld))
+
+    def info(self) -> dict:
+        i = PlanInfo()
+        _check(lib().rdx_plan_get_info(self._h, ctypes.byref(i)))
+        return {n: getattr(i, n) for n, _ in PlanInfo._fields_}
+
+    def view(self) -> dict:
+        v = PlanView()
+        _check(lib().rdx_plan_get_view(self._h, ctypes.byref(v)))
+
+        def arr(p, n, w):
+            if n == 0:
+                return np.zeros((0, w), np.int32)
+            return np.ctypeslib.as_array(p, shape=(n * w,)).reshape(n, w).copy()
+
+        return dict(items=arr(v.items, v.num_items, 8), tiles=arr(v.tiles, v.num_tiles, 8),
+                    jobs=arr(v.jobs, v.num_jobs, 8), tokens=arr(v.tokens, v.num_tokens, 2),
+                    contribs=arr(v.contribs, v.num_contribs, 4), tile_rows=v.tile_rows, group=v.group)
+
+    def upload(self, dev_plan, dev_plan_bytes: int, page_table, page_table_rows: int, stream=None):
+        _check(lib().rdx_plan_upload(self._h, _ptr(dev_plan), dev_plan_bytes, _ptr(page_table),
+                                     page_table_rows, _stream(stream)))
+
+
+# ------------------------------------------------------------- device ops
+def kv_store(desc: AttnDesc, k_pool, v_pool, k_new, v_new, slots, n: int, stream=None):
+    _check(lib().rdx_kv_store(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                              _ptr(slots), n, _stream(stream)))
+
+
+def extend_attention(desc: AttnDesc, plan: Plan, dev_plan, q, k_pool, v_pool, page_table, o,
+                     workspace, workspace_bytes: int, stream=None):
+    _check(lib().rdx_extend_attention(ctypes.byref(desc), plan.handle, _ptr(dev_plan), _ptr(q), _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(page_table), _ptr(o), _ptr(workspace),
+                                      workspace_bytes, _stream(stream)))
+
+
+def decode_attention(desc: AttnDesc, plan: Plan, dev_plan, q, k_pool, v_pool, page_table, o,
+                     workspace, workspace_bytes: int, stream=None):
+    _check(lib().rdx_decode_attention(ctypes.byref(desc), plan.handle, _ptr(dev_plan), _ptr(q), _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(page_table), _ptr(o), _ptr(workspace),
+                                      workspace_bytes, _stream(stream)))
+
+
+def timing_begin(cap: int):
+    _check(lib().rdx_timing_begin(cap))
+
+
+def timing_read(cap: int):
+    """-> (durations_ms np.float32[n], kinds np.int32[n]) of the launches recorded since timing_begin."""
+    ms = np.zeros(max(cap, 1), np.float32)
+    kinds = np.zeros(max(cap, 1), np.int32)
+    n = i32()
+    _check(lib().rdx_timing_read(ms.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _p32(kinds), cap,
+                                 ctypes.byref(n)))
+    return ms[: n.value].copy(), kinds[: n.value].copy()

@@ -1,0 +1,89 @@
+"""The C-ABI library loads without a GPU and exports every function that
+include/rdx.h declares; error paths report codes and leave state unchanged."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from prefix_shared_kv_token_amd import rdx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "rdx.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(rdx_\w+)\s*\(", text))
+
+
+def test_header_matches_binding_and_exports():
+    declared = _declared()
+    assert declared == set(rdx.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", rdx.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (rdx_\w+)", out))
+    assert declared <= exported, declared - exported
+    lib = rdx.lib()
+    for name in declared:
+        assert getattr(lib, name) is not None
+    assert lib.rdx_version().decode().startswith("rdx")
+
+
+def test_tree_errors():
+    with pytest.raises(rdx.RdxError) as e:
+        rdx.Tree(0)
+    assert e.value.code == rdx.EINVAL
+    t = rdx.Tree(4)
+    with pytest.raises(rdx.RdxError) as e:
+        t.lock(99)
+    assert e.value.code == rdx.ESTATE
+    s = t.alloc(4)
+    with pytest.raises(rdx.RdxError) as e:
+        t.alloc(1)
+    assert e.value.code == rdx.ENOSPC
+    assert t.stats()["private"] == 4
+    t.free(s[:2])
+    with pytest.raises(rdx.RdxError) as e:
+        t.free(s[:1])
+    assert e.value.code == rdx.ESTATE
+    with pytest.raises(rdx.RdxError) as e:
+        t.free([7])
+    assert e.value.code == rdx.EINVAL
+    with pytest.raises(rdx.RdxError) as e:
+        t.insert([1, 2], [s[2], s[2]])          # slot listed twice
+    assert e.value.code == rdx.ESTATE
+    assert t.stats()["cached"] == 0 and t.stats()["clock"] == 0
+
+
+def test_descriptor_errors():
+    with pytest.raises(rdx.RdxError) as e:
+        rdx.Plan(rdx.attn_desc(rdx.BF16, 32, 8, 96, 100), rdx.PLAN_EXTEND)
+    assert e.value.code == rdx.EUNSUPPORTED
+    with pytest.raises(rdx.RdxError) as e:
+        rdx.Plan(rdx.attn_desc(rdx.BF16, 30, 8, 128, 100), rdx.PLAN_EXTEND)
+    assert e.value.code == rdx.EINVAL
+    with pytest.raises(rdx.RdxError) as e:
+        rdx.Plan(rdx.attn_desc(7, 32, 8, 128, 100), rdx.PLAN_EXTEND)
+    assert e.value.code == rdx.EUNSUPPORTED
+    with pytest.raises(rdx.RdxError) as e:
+        rdx.Plan(rdx.attn_desc(rdx.BF16, 32, 8, 128, 100), 5)
+    assert e.value.code == rdx.EINVAL
+
+
+def test_plan_build_rejects_inconsistent_batches():
+    t = rdx.Tree(64)
+    m, slots, node = t.match_prefix(np.arange(10))
+    new = t.alloc(10)
+    p = rdx.Plan(rdx.attn_desc(rdx.BF16, 8, 2, 128, 64), rdx.PLAN_EXTEND)
+    p.build(t, [node], [0], [10], [10], [0], new, 16)
+    assert p.info()["num_new"] == 10
+    with pytest.raises(rdx.RdxError):                      # kv_len beyond the row stride
+        p.build(t, [node], [0], [20], [10], [0], new, 16)
+    with pytest.raises(rdx.RdxError):                      # two requests on one row
+        p.build(t, [node, node], [0, 0], [5, 5], [5, 5], [0, 0], new, 16)
+    with pytest.raises(rdx.RdxError):                      # slot outside the pool
+        p.build(t, [node], [0], [1], [1], [0], [64], 16)
+    with pytest.raises(rdx.RdxError) as e:                 # unknown node
+        p.build(t, [12345], [0], [1], [1], [0], [3], 16)
+    assert e.value.code == rdx.ESTATE

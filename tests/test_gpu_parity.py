@@ -1,0 +1,141 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Match lengths and page-table rows must be bit-exact; attention outputs
+within max-abs 1e-4 (fp32 workloads) or 2e-2 (bf16 workloads, fp32
+accumulation).  Small shapes are checked on every output; the five full-size
+workloads run exactly as the benchmark runs them and are checked on sampled
+requests the oracle computes one by one."""
+import numpy as np
+import pytest
+
+from oracle import run_workload
+from workloads import CONFIGS, Workload, config_by_name
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _fragmenter(num_slots, keep, seed):
+    def prep(cache):
+        rng = np.random.default_rng(seed)
+        allslots = np.asarray(cache.alloc(num_slots))
+        cache.free(np.sort(rng.choice(allslots, keep, replace=False)))
+    return prep
+
+
+def run_and_check(cfg, sample_leaves=None, extend_items=0, decode_items=0, hole_seed=None, extra_slots=0):
+    torch = _torch()
+    from prefix_shared_kv_token_amd.driver import WorkloadRun
+
+    wl = Workload(cfg)
+    print(f"\n[gpu] {cfg.name} levels={cfg.levels} Hq/Hkv={cfg.n_q_heads}/{cfg.n_kv_heads} D={cfg.head_dim} "
+          f"{cfg.dtype} items={extend_items}/{decode_items} holes={hole_seed}", flush=True)
+    run = WorkloadRun(wl, extend_items=extend_items, decode_items=decode_items, hole_seed=hole_seed,
+                      extra_slots=extra_slots)
+    out = run.run()
+    torch.cuda.synchronize()
+    leaves = wl.leaf_requests
+    if sample_leaves is None:
+        rids = [r.rid for r in wl.all_requests]
+    else:
+        idx = sorted(set(int(i) % len(leaves) for i in sample_leaves))
+        rids = [leaves[i].rid for i in idx] + [wl.phases[0].requests[0].rid]
+    prep = _fragmenter(run.num_slots, cfg.total_tokens(), hole_seed) if hole_seed is not None else None
+    ref = run_workload(wl, num_slots=run.num_slots, attention_for=rids, prepare=prep)
+    # ---- indices: bit-exact ----
+    for pi, ph in enumerate(wl.phases):
+        for j, r in enumerate(ph.requests):
+            assert out["matched"][pi][j] == ref.matched[r.rid], (pi, j)
+            np.testing.assert_array_equal(out["rows"][pi][j], ref.rows[r.rid])
+    # ---- outputs ----
+    tol = TOL[cfg.dtype]
+    worst = 0.0
+    for pi, ph in enumerate(wl.phases):
+        off = 0
+        for j, r in enumerate(ph.requests):
+            if r.rid in ref.extend_out:
+                got = out["extend"][pi][off:off + r.own_len].float().cpu().numpy()
+                err = float(np.abs(got - ref.extend_out[r.rid]).max())
+                worst = max(worst, err)
+                assert err <= tol, f"extend phase {pi} request {j}: max abs err {err}"
+                if r.decode_steps:
+                    gd = out["decode"][:, j].float().cpu().numpy()
+                    err = float(np.abs(gd - ref.decode_out[r.rid]).max())
+                    worst = max(worst, err)
+                    assert err <= tol, f"decode request {j}: max abs err {err}"
+            off += r.own_len
+    print(f"[gpu] {cfg.name}: {len(rids)} requests checked, max abs err {worst:.3g} (tol {tol})", flush=True)
+    return run, out, ref
+
+
+def test_tiny_all_outputs():
+    run_and_check(config_by_name("tiny"))
+
+
+def test_tiny_split_items_and_fragmented_pool():
+    cfg = config_by_name("tiny")
+    run_and_check(cfg, extend_items=100000, decode_items=100000, hole_seed=5, extra_slots=97)
+
+
+EDGE = [
+    # bf16 head_dim 64, GQA 4, ragged suffix
+    ("tiny", dict(levels=((2, 150), (3, 37)), n_q_heads=8, n_kv_heads=2, dtype="bf16", sigma=0.5, decode_steps=5)),
+    # one-token suffixes
+    ("batchllm", dict(levels=((2, 200), (6, 1)), decode_steps=3)),
+    # no shared prefix at all (every request is its own hint), MHA
+    ("helpdesk", dict(levels=((5, 77),), n_q_heads=4, n_kv_heads=4, decode_steps=4)),
+    # a prefix reached by a single request degrades to its own range
+    ("batchllm", dict(levels=((3, 100), (1, 20)), decode_steps=2)),
+    # fp32, GQA, three levels
+    ("tiny", dict(levels=((1, 40), (3, 17), (2, 9)), n_q_heads=8, n_kv_heads=2, head_dim=128, decode_steps=6)),
+    # GQA 8 (group of 8 query heads per KV head)
+    ("longprefix", dict(levels=((2, 300), (4, 33)), n_q_heads=16, n_kv_heads=2, decode_steps=3)),
+]
+
+
+@pytest.mark.parametrize("base,kw", EDGE, ids=[f"{b}-{i}" for i, (b, _) in enumerate(EDGE)])
+@pytest.mark.parametrize("items", [0, 100000], ids=["fused", "split"])
+def test_edge_shapes(base, kw, items):
+    run_and_check(config_by_name(base).replace(**kw), extend_items=items, decode_items=items)
+
+
+def test_fragmented_pool_bf16():
+    cfg = config_by_name("multilevel").replace(levels=((1, 100), (2, 40), (3, 11)), decode_steps=4)
+    run_and_check(cfg, hole_seed=11, extra_slots=333)
+
+
+def test_deterministic_and_kv_store_roundtrip():
+    torch = _torch()
+    from prefix_shared_kv_token_amd.driver import WorkloadRun
+
+    cfg = config_by_name("batchllm").replace(levels=((2, 130), (4, 21)), decode_steps=3)
+    wl = Workload(cfg)
+    run = WorkloadRun(wl)
+    a = run.run()
+    b = run.run()
+    torch.cuda.synchronize()
+    for x, y in zip(a["extend"], b["extend"]):
+        assert torch.equal(x, y)
+    assert torch.equal(a["decode"], b["decode"])
+    # the pool holds every stored token's K/V at its slot
+    leaf = wl.leaf_requests[1]
+    row = a["rows"][-1][1]
+    k_log, v_log = wl.request_full_kv(leaf)
+    kp = run.rt.k_pool[torch.as_tensor(row, device=run.rt.device).long()].float().cpu().numpy()
+    vp = run.rt.v_pool[torch.as_tensor(row, device=run.rt.device).long()].float().cpu().numpy()
+    np.testing.assert_array_equal(kp, k_log)
+    np.testing.assert_array_equal(vp, v_log)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS[1:], ids=lambda c: c.name)
+def test_full_size_sampled(cfg):
+    """Full-size workloads, default launch configuration (as timed by the
+    benchmark), checked on sampled leaf requests plus the first hint."""
+    run_and_check(cfg, sample_leaves=[0, 1, 17, -1])

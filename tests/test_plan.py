@@ -1,0 +1,143 @@
+"""Host-side properties of the batch planner (no GPU needed).
+
+For every new token and KV head, the key positions assigned to it over all
+work items and jobs must be exactly {0, ..., its position}, each once;
+shared segments must be read once per tile instead of once per request;
+tiles, contributions and workspace offsets must be consistent."""
+import numpy as np
+import pytest
+
+from prefix_shared_kv_token_amd import rdx
+from workloads import Workload, config_by_name
+
+
+def _admit_phases(cfg, kind_last="extend"):
+    """Runs the admission protocol of every phase on the C++ tree and returns
+    the plan inputs of the last extend phase and of one decode step."""
+    wl = Workload(cfg)
+    tree = rdx.Tree(cfg.total_tokens())
+    out = []
+    for pi, ph in enumerate(wl.phases):
+        reqs = []
+        for r in ph.requests:
+            p = wl.prompt_tokens(r)
+            m, slots, node = tree.match_prefix(p)
+            tree.lock(node)
+            new = tree.alloc(len(p) - m).copy()
+            reqs.append((p, m, node, np.concatenate([slots, new])))
+        out.append(reqs)
+        if pi < len(wl.phases) - 1:
+            for p, m, node, row in reqs:
+                k, _ = tree.insert(p, row)
+                tree.free(row[m:k])
+                tree.unlock(node)
+    return wl, tree, out
+
+
+def _check_coverage(plan, kv_len, q_len, rows, hkv):
+    v = plan.view()
+    group = v["group"]
+    items, tiles, jobs, toks, contribs = v["items"], v["tiles"], v["jobs"], v["tokens"], v["contribs"]
+    row_of_req = {r: i for i, r in enumerate(rows)}
+    # which request owns a q index, and its position
+    q_off = np.concatenate([[0], np.cumsum(q_len)])
+    n_tok = int(q_off[-1])
+    cover = {}
+    seen_tok = np.zeros(n_tok, int)
+    for t in tiles:
+        assert 0 < t[1] * group <= v["tile_rows"]
+        for j in range(t[0], t[0] + t[1]):
+            seen_tok[toks[j, 0]] += 1
+    assert (seen_tok == 1).all()
+    for it in items:
+        tile = tiles[it[0]]
+        kvh = it[1]
+        assert 0 <= kvh < hkv
+        if tile[2] > 1:
+            c = contribs[tile[3] + it[4]]
+        for jb in range(it[2], it[3]):
+            j = jobs[jb]
+            for tl in range(j[3], j[4]):
+                qi, pos = toks[tile[0] + tl]
+                if tile[2] > 1:
+                    assert c[0] <= tl < c[1]
+                r = int(np.searchsorted(q_off, qi, side="right") - 1)
+                end = min(j[2], pos + 1) if j[5] else j[2]
+                for p in range(j[1], end):
+                    key = (qi, kvh, p)
+                    cover[key] = cover.get(key, 0) + 1
+                # the job reads the row of a request that shares these positions
+                assert j[0] in row_of_req
+    for qi in range(n_tok):
+        r = int(np.searchsorted(q_off, qi, side="right") - 1)
+        pos = kv_len[r] - q_len[r] + (qi - q_off[r])
+        for h in range(hkv):
+            got = sorted(p for (a, b, p), c in cover.items() if a == qi and b == h for _ in range(c))
+            assert got == list(range(pos + 1)), (qi, h)
+    return v
+
+
+@pytest.mark.parametrize("name,levels,decode", [
+    ("batchllm", ((3, 40), (5, 13)), 3),
+    ("helpdesk", ((1, 70), (9, 7)), 2),
+    ("multilevel", ((1, 20), (3, 9), (2, 5)), 2),
+    ("tiny", ((1, 0 + 8), (3, 1)), 1),
+])
+@pytest.mark.parametrize("target", [0, 1, 4096])
+def test_extend_and_decode_plans_cover_each_visible_key_once(name, levels, decode, target):
+    cfg = config_by_name(name).replace(levels=levels, decode_steps=decode, n_q_heads=8, n_kv_heads=2)
+    wl, tree, phases = _admit_phases(cfg)
+    reqs = phases[-1]
+    desc = rdx.attn_desc(rdx.BF16, 8, 2, 128, cfg.total_tokens())
+    ld = cfg.max_seq_len
+    rows = list(range(len(reqs)))
+    # extend of the last phase
+    plan = rdx.Plan(desc, rdx.PLAN_EXTEND, target)
+    kv_len = [len(p) for p, *_ in reqs]
+    q_len = [len(p) - m for p, m, *_ in reqs]
+    new = np.concatenate([row[m:] for p, m, n, row in reqs])
+    plan.build(tree, [n for _, _, n, _ in reqs], rows, kv_len, q_len, [0] * len(reqs), new, ld)
+    _check_coverage(plan, kv_len, q_len, rows, 2)
+    info = plan.info()
+    assert info["num_new"] == sum(q_len)
+    # one decode step
+    dplan = rdx.Plan(desc, rdx.PLAN_DECODE, target)
+    slots = tree.alloc(len(reqs))
+    kv1 = [k + 1 for k in kv_len]
+    dplan.build(tree, [n for _, _, n, _ in reqs], rows, kv1, [1] * len(reqs), kv_len, slots, ld)
+    v = _check_coverage(dplan, kv1, [1] * len(reqs), rows, 2)
+    # a shared prefix is attended once per decode tile, not once per request
+    n_shared = dplan.info()["num_shared_segments"]
+    assert n_shared >= 1
+    shared_jobs = [j for j in v["jobs"] if j[5] == 0]
+    shared_keys = sum(j[2] - j[1] for j in shared_jobs)
+    prefix = sum(length for _, length in levels[:-1])
+    assert shared_keys <= prefix * len(v["tiles"]) * (len(levels) - 1)
+    if target == 4096 and sum(j[2] - j[1] for j in v["jobs"]) > 64 * len(v["tiles"]):
+        assert dplan.info()["num_split_tiles"] > 0 and dplan.info()["workspace_bytes"] > 0
+
+
+def test_single_request_groups_degrade_to_own_ranges():
+    """A prefix node reached by one request of the batch is not shared."""
+    cfg = config_by_name("batchllm").replace(levels=((4, 30), (1, 10)), decode_steps=1, n_q_heads=8, n_kv_heads=2)
+    wl, tree, phases = _admit_phases(cfg)
+    reqs = phases[-1]
+    desc = rdx.attn_desc(rdx.BF16, 8, 2, 128, cfg.total_tokens())
+    plan = rdx.Plan(desc, rdx.PLAN_EXTEND)
+    kv_len = [len(p) for p, *_ in reqs]
+    q_len = [len(p) - m for p, m, *_ in reqs]
+    new = np.concatenate([row[m:] for p, m, n, row in reqs])
+    plan.build(tree, [n for _, _, n, _ in reqs], list(range(len(reqs))), kv_len, q_len, [0] * len(reqs), new, 64)
+    assert plan.info()["num_shared_segments"] == 0
+    _check_coverage(plan, kv_len, q_len, list(range(len(reqs))), 2)
+
+
+def test_empty_batch_and_zero_query_requests():
+    desc = rdx.attn_desc(rdx.BF16, 4, 4, 64, 16)
+    tree = rdx.Tree(16)
+    plan = rdx.Plan(desc, rdx.PLAN_DECODE)
+    plan.build(tree, [], [], [], [], [], [], 8)
+    assert plan.info()["num_items"] == 0
+    s = tree.alloc(3)
+    plan.build(tree, [0, 0], [0, 1], [3, 0], [3, 0], [0, 0], s, 8)
+    assert plan.info()["num_new"] == 3 and plan.info()["num_tiles"] == 1

@@ -7,9 +7,11 @@ Recipe (the same for every consumer):
   * token ids are uniform integers in [0, vocab); the first token of a
     segment is redrawn until it differs from the first tokens of all its
     sibling segments, so the sharing tree is exactly the intended one;
-  * Q, K and V are N(0, 1) * sigma drawn in float32; for bf16 workloads they
-    are then rounded to bfloat16 (round to nearest even) and both sides consume
-    the rounded values (the GPU as bf16 bits, the oracle upcast to fp64).
+  * Q, K and V are N(0, 1) * sigma drawn in float32 with torch's CPU
+    generator (seeded from the same SeedSequence; its output does not depend
+    on the thread count); for bf16 workloads they are then rounded to
+    bfloat16 (round to nearest even) and both sides consume the rounded values
+    (the GPU as bf16, the oracle upcast to fp64).
 K/V belong to a *logical* token (sharing-tree node, offset), so a shared
 prefix has one set of keys/values however many requests reuse it.
 """
@@ -19,6 +21,7 @@ import functools
 from dataclasses import dataclass, field
 
 import numpy as np
+import torch
 
 from .configs import Config
 
@@ -143,12 +146,18 @@ class Workload:
         return rng.integers(0, self.cfg.vocab, size=req.decode_steps, dtype=np.int64).astype(np.int32)
 
     # ---------------- values ----------------
-    def _normal(self, shape, *ids) -> np.ndarray:
-        x = self._rng(*ids).standard_normal(shape, dtype=np.float32)
-        x *= np.float32(self.cfg.sigma)
+    def _normal_t(self, shape, *ids) -> torch.Tensor:
+        """float32 torch tensor (bf16-representable for bf16 workloads)."""
+        seed = int(np.random.SeedSequence([SEED, self.cfg.index, *ids]).generate_state(1, np.uint64)[0]) >> 1
+        g = torch.Generator().manual_seed(seed)
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        x *= self.cfg.sigma
         if self.cfg.dtype == "bf16":
-            x = bf16_bits_to_f32(bf16_round_bits(x))
+            x = x.to(torch.bfloat16).to(torch.float32)
         return x
+
+    def _normal(self, shape, *ids) -> np.ndarray:
+        return self._normal_t(shape, *ids).numpy()
 
     @functools.lru_cache(maxsize=256)
     def node_kv(self, node_id: int):
@@ -171,33 +180,47 @@ class Workload:
         shape = (req.decode_steps, c.n_kv_heads, c.head_dim)
         return self._normal(shape, TAG_DK, req.rid), self._normal(shape, TAG_DV, req.rid)
 
-    # ---------------- stacked per-phase arrays (for bulk upload) ----------------
-    def phase_arrays(self, phase: Phase):
-        """Concatenated new-token arrays of an extend phase, request-major:
-        q [sum own_len, Hq, D], k, v [sum own_len, Hkv, D] (float32)."""
-        qs, ks, vs = [], [], []
-        for r in phase.requests:
-            qs.append(self.request_q(r))
-            k, v = self.node_kv(r.node)
-            ks.append(k)
-            vs.append(v)
-        return np.concatenate(qs), np.concatenate(ks), np.concatenate(vs)
+    # ---------------- bulk fill (for device upload) ----------------
+    def _fill(self, dst: torch.Tensor, shape, *ids):
+        """Draw one piece and copy it into `dst` (any dtype / device), through
+        a reused host buffer so large workloads do not churn host memory."""
+        n = int(np.prod(shape))
+        buf = getattr(self, "_scratch", None)
+        if buf is None or buf.numel() < n:
+            buf = torch.empty(max(n, 1 << 20), dtype=torch.float32)
+            self._scratch = buf
+        seed = int(np.random.SeedSequence([SEED, self.cfg.index, *ids]).generate_state(1, np.uint64)[0]) >> 1
+        x = buf[:n].view(shape)
+        torch.randn(shape, generator=torch.Generator().manual_seed(seed), out=x)
+        x *= self.cfg.sigma
+        dst.copy_(x)          # to bf16: round to nearest even, as the oracle's copy
 
-    def decode_arrays(self):
-        """Decode inputs for all leaf requests, step-major:
-        tokens [T, R], q [T, R, Hq, D], k, v [T, R, Hkv, D] (float32)."""
-        reqs = self.leaf_requests
+    def fill_phase(self, phase: Phase, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        """New-token arrays of an extend phase, request-major, written into
+        q [sum own_len, Hq, D] and k, v [sum own_len, Hkv, D]."""
         c = self.cfg
-        T, R = c.decode_steps, len(reqs)
-        tok = np.empty((T, R), np.int32)
-        q = np.empty((T, R, c.n_q_heads, c.head_dim), np.float32)
-        k = np.empty((T, R, c.n_kv_heads, c.head_dim), np.float32)
-        v = np.empty_like(k)
-        for j, r in enumerate(reqs):
-            tok[:, j] = self.decode_tokens(r)
-            q[:, j] = self.decode_q(r)
-            k[:, j], v[:, j] = self.decode_kv(r)
-        return tok, q, k, v
+        off = 0
+        for r in phase.requests:
+            n = r.own_len
+            self._fill(q[off:off + n], (n, c.n_q_heads, c.head_dim), TAG_Q, r.rid)
+            self._fill(k[off:off + n], (n, c.n_kv_heads, c.head_dim), TAG_K, r.node)
+            self._fill(v[off:off + n], (n, c.n_kv_heads, c.head_dim), TAG_V, r.node)
+            off += n
+
+    def fill_decode(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        """Decode inputs of the leaf requests, step-major: q [T, R, Hq, D],
+        k, v [T, R, Hkv, D]."""
+        c = self.cfg
+        T = c.decode_steps
+        for j, r in enumerate(self.leaf_requests):
+            self._fill(q[:, j], (T, c.n_q_heads, c.head_dim), TAG_DQ, r.rid)
+            self._fill(k[:, j], (T, c.n_kv_heads, c.head_dim), TAG_DK, r.rid)
+            self._fill(v[:, j], (T, c.n_kv_heads, c.head_dim), TAG_DV, r.rid)
+
+    def decode_token_matrix(self) -> np.ndarray:
+        """Decode token ids of the leaf requests, [R, T]."""
+        return np.stack([self.decode_tokens(r) for r in self.leaf_requests]) if self.leaf_requests else \
+            np.zeros((0, self.cfg.decode_steps), np.int32)
 
     def request_full_kv(self, req: Request, n_decode: int | None = None):
         """Logical K/V of the request's whole sequence: its path nodes, then
