@@ -193,7 +193,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, default=float), flush=True)
 
 
 if __name__ == "__main__":

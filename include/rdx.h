@@ -223,14 +223,16 @@ int rdx_plan_get_view(const rdx_plan* plan, rdx_plan_view* out);
 /* Prefix-shared attention of one plan (extend or decode kind respectively):
  * for every new token at position p and query head h,
  *   O[tok][h] = softmax_j(scale * q.k_j) v_j  over positions j <= p of its row,
- * reading K/V through the page table.  One launch: work items cover
- * (row tile, KV head, key range); tiles whose key ranges were split merge
- * their partial (o, max, sum) states by log-sum-exp in the same launch (the
- * last item to finish merges).  q/o: device [sum q_len][Hq][head_dim] in
- * caller order.  workspace: device, >= workspace_bytes, zero-filled once
- * before its first use (every launch leaves its counters at zero again);
- * may be NULL when workspace_bytes == 0.  Launches that share a workspace
- * must not overlap.  Errors: EINVAL, EUNSUPPORTED, EDEVICE. */
+ * reading K/V through the page table.  Work items cover (row tile, KV head,
+ * key ranges); a tile streams its shared-prefix keys and its requests' own
+ * keys with one online-softmax state.  Tiles whose key ranges the planner
+ * split over several items write partial (o, max, sum) states to the
+ * workspace, and a merge kernel enqueued right behind combines them by
+ * log-sum-exp.  q/o: device [sum q_len][Hq][head_dim] in caller order.
+ * workspace: device scratch for the partial states, >= workspace_bytes, no
+ * initial contents needed; may be NULL when workspace_bytes == 0.  Launches
+ * sharing a workspace must be stream-ordered.  Errors: EINVAL, EUNSUPPORTED,
+ * EDEVICE. */
 int rdx_extend_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const void* dev_plan,
                          const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, void* o, void* workspace,

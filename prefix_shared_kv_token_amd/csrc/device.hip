@@ -3,11 +3,14 @@
 //
 // Attention follows the BatchLLM explainer, Horizontal Fusion section: the
 // common-prefix part and each request's own part of prefix-shared attention
-// run as different workgroups of one kernel, and their partial results are
-// combined in that launch.  The partial softmax states (o, running max m,
-// running sum l) are combined with the log-sum-exp rule
+// are work of one kernel -- a row tile streams the shared-prefix keys and its
+// requests' own keys, carrying one online-softmax state across both -- and
+// when a tile's key ranges are split over several workgroups, their partial
+// softmax states (o, running max m, running sum l) are combined with the
+// log-sum-exp rule
 //   M = max_c m_c,  w_c = l_c 2^(m_c - M),  o = sum_c w_c o_c / sum_c w_c
-// (scores kept in the base-2 domain: t = s * scale * log2 e).
+// (scores kept in the base-2 domain: t = s * scale * log2 e) by a merge pass
+// queued right behind the attention kernel.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -21,6 +24,7 @@
 namespace rdx {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -32,13 +36,13 @@ struct AttnArgs {
   const int32_t* jobs;
   const int32_t* toks;
   const int32_t* contribs;
+  const int32_t* splits;
   const int32_t* page_table;
   int64_t ld;
   const void* q;
   const void* kp;
   const void* vp;
   void* o;
-  int32_t* counters;
   float* ws_o;
   float* ws_ml;
   int64_t ws_tokens;
@@ -52,19 +56,20 @@ __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(__bf16* p, float v) { *p = (__bf16)v; }
 
 // ---------------------------------------------------------------------------
-// Partial-state epilogue shared by both kernels.
-//
-// A contribution's partial for (tile token t, grouped head hh) lives at
+// Merge of split tiles.  A contribution's partial for (tile token t, grouped
+// head hh) lives at
 //   ws_o [((kvh * ws_tokens + base + t - lo) * group + hh) * D + d]
-//   ws_ml[((kvh * ws_tokens + base + t - lo) * group + hh) * 2 + {0:m, 1:l}]
-// with o already normalised by its own l.
+//   ws_ml[((kvh * ws_tokens + base + t - lo) * group + hh) * 2 + {0: m, 1: l}]
+// with o already normalised by its own l.  One workgroup per (split tile,
+// KV head); it runs after the attention kernel in stream order.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__device__ void merge_tile(const AttnArgs& a, const int32_t* tile, int kvh) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
+  const int32_t* tile = a.tiles + (int64_t)a.splits[blockIdx.x / a.hkv] * kTileWords;
+  const int kvh = blockIdx.x % a.hkv;
   const int n_tok = tile[1], n_contrib = tile[2], cbeg = tile[3];
   const int group = a.group;
   const int n_rows = n_tok * group;
-  const int64_t hq = a.hq;
   T* out = reinterpret_cast<T*>(a.o);
   constexpr int kVec = 4;
   constexpr int kPer = D / kVec;  // float4 columns per row
@@ -75,7 +80,7 @@ __device__ void merge_tile(const AttnArgs& a, const int32_t* tile, int kvh) {
     for (int c = 0; c < n_contrib; ++c) {
       const int32_t* cr = a.contribs + (int64_t)(cbeg + c) * kContribWords;
       if (t < cr[0] || t >= cr[1]) continue;
-      int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
+      const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
       mmax = fmaxf(mmax, a.ws_ml[w * 2]);
     }
     float acc[kVec] = {0.f, 0.f, 0.f, 0.f};
@@ -83,11 +88,11 @@ __device__ void merge_tile(const AttnArgs& a, const int32_t* tile, int kvh) {
     for (int c = 0; c < n_contrib; ++c) {
       const int32_t* cr = a.contribs + (int64_t)(cbeg + c) * kContribWords;
       if (t < cr[0] || t >= cr[1]) continue;
-      int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
-      float l = a.ws_ml[w * 2 + 1];
+      const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
+      const float l = a.ws_ml[w * 2 + 1];
       if (l <= 0.f) continue;
-      float wt = l * exp2_fast(a.ws_ml[w * 2] - mmax);
-      float4 v = *reinterpret_cast<const float4*>(a.ws_o + w * D + col);
+      const float wt = l * exp2_fast(a.ws_ml[w * 2] - mmax);
+      const float4 v = *reinterpret_cast<const float4*>(a.ws_o + w * D + col);
       acc[0] += wt * v.x;
       acc[1] += wt * v.y;
       acc[2] += wt * v.z;
@@ -96,30 +101,42 @@ __device__ void merge_tile(const AttnArgs& a, const int32_t* tile, int kvh) {
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     const int32_t q_index = a.toks[(int64_t)(tile[0] + t) * kTokWords];
-    T* dst = out + ((int64_t)q_index * hq + (int64_t)kvh * group + hh) * D + col;
+    T* dst = out + ((int64_t)q_index * a.hq + (int64_t)kvh * group + hh) * D + col;
 #pragma unroll
     for (int e = 0; e < kVec; ++e) store_out(dst + e, acc[e] * inv);
   }
 }
 
-// Called by every thread after its partial rows are stored; the last of the
-// tile's contributions to arrive merges them all and resets the counter.
-template <typename T, int D>
-__device__ void arrive_and_merge(const AttnArgs& a, const int32_t* tile, int kvh, int* s_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t* ctr = a.counters + (int64_t)tile[4] * a.hkv + kvh;
-    int prev = atomicAdd(ctr, 1);
-    int last = prev == tile[2] - 1;
-    if (last) *ctr = 0;  // every contribution has arrived: ready for the next launch
-    *s_flag = last;
-  }
-  __syncthreads();
-  if (*s_flag) {
-    __threadfence();
-    merge_tile<T, D>(a, tile, kvh);
-  }
+// ---------------------------------------------------------------------------
+// Iteration over the 64-key blocks of a work item's jobs.
+// ---------------------------------------------------------------------------
+struct BlockIter {
+  int j, kb, k1;
+  const int32_t* prow;
+};
+
+__device__ __forceinline__ void iter_job(const AttnArgs& a, BlockIter& it, int j) {
+  const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+  it.j = j;
+  it.prow = a.page_table + (int64_t)job[0] * a.ld;
+  it.kb = job[1];
+  it.k1 = job[2];
+}
+
+__device__ __forceinline__ void iter_next(const AttnArgs& a, BlockIter& it, int je) {
+  it.kb += 64;
+  if (it.kb >= it.k1 && it.j + 1 < je) iter_job(a, it, it.j + 1);
+}
+
+// slots of keys 4qd .. 4qd+3 of the block (-1 past the job's end)
+__device__ __forceinline__ int4 load_slots(const BlockIter& it, int qd) {
+  const int p = it.kb + 4 * qd;
+  int4 s;
+  s.x = p < it.k1 ? it.prow[p] : -1;
+  s.y = p + 1 < it.k1 ? it.prow[p + 1] : -1;
+  s.z = p + 2 < it.k1 ? it.prow[p + 2] : -1;
+  s.w = p + 3 < it.k1 ? it.prow[p + 3] : -1;
+  return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -132,31 +149,43 @@ __device__ void arrive_and_merge(const AttnArgs& a, const int32_t* tile, int kvh
 // registers.  The contraction order inside a 16-key step is permuted
 // identically on both operands: lane half h holds keys {4h..4h+3, 8+4h..
 // 8+4h+3}; V^T is stored in LDS with its key quads in that order.
+//
+// Pipeline: page-table slots are fetched two key blocks ahead and K/V rows
+// one block ahead into registers while the MFMAs of the current block run;
+// K and V^T live in a double-buffered LDS tile, one barrier per block.
 // ---------------------------------------------------------------------------
 template <int D>
-struct SmemBF16 {
+struct KVTile {
   static constexpr int KS = D + 8;   // K tile row stride (elements), padded
   static constexpr int VS = 64 + 8;  // V^T tile row stride
   __bf16 k[64 * KS];
   __bf16 vt[D * VS];
-  int32_t slot[64];
-  int flag;
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ SmemBF16<D> sm;
-  constexpr int KS = SmemBF16<D>::KS, VS = SmemBF16<D>::VS;
+  __shared__ KVTile<D> buf[2];
+  constexpr int KS = KVTile<D>::KS, VS = KVTile<D>::VS;
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over head_dim
   constexpr int DB = D / 32;      // 32-wide d blocks of the output
+  constexpr int CH = D / 8;       // 16-byte chunks per K/V row
+  constexpr int UNITS = 16 * CH;  // (key quad, chunk) units per matrix
+  constexpr bool BOTH = 2 * UNITS > kThreads;  // each thread loads K and V of one unit
+
+  const int tid = threadIdx.x;
+  const int uu = BOTH ? tid : tid % UNITS;
+  const bool doK = BOTH || tid < UNITS;
+  const bool doV = BOTH || tid >= UNITS;
+  const int qd = uu / CH, cc = uu % CH;
 
   const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
   const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
   const int kvh = item[1];
+  const int jb = item[2], je = item[3];
   const int tok_begin = tile[0], n_tok = tile[1];
   const int group = a.group;
   const int n_rows = n_tok * group;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hi = lane >> 5;
   const int row = wave * 32 + li;  // this lane's query row in the tile
   const bool row_ok = row < n_rows;
@@ -188,113 +217,149 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
   const __bf16* kpool = reinterpret_cast<const __bf16*>(a.kp);
   const __bf16* vpool = reinterpret_cast<const __bf16*>(a.vp);
-  constexpr int CH = D / 8;        // 16-byte chunks per K/V row
-  constexpr int UNITS = 16 * CH;   // (key quad, chunk) units per matrix
+  const int64_t head_off = (int64_t)kvh * D + 8 * cc;
+  const int64_t slot_stride = (int64_t)a.hkv * D;
 
-  for (int j = item[2]; j < item[3]; ++j) {
+  int nblk = 0;
+  for (int j = jb; j < je; ++j) {
     const int32_t* job = a.jobs + (int64_t)j * kJobWords;
-    const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
-    const int k0 = job[1], k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
-    // keys visible to this lane: positions < lim
-    int lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
-    const bool wave_job = wave_live && __ballot(lim > k0) != 0;
-    for (int kb = k0; kb < k1; kb += 64) {
-      if (threadIdx.x < 64) {
-        int p = kb + threadIdx.x;
-        sm.slot[threadIdx.x] = p < k1 ? prow[p] : -1;
-      }
-      __syncthreads();
-      for (int u = threadIdx.x; u < 2 * UNITS; u += kThreads) {
-        const int which = u / UNITS, uu = u % UNITS, qd = uu / CH, c = uu % CH;
-        const __bf16* base = which ? vpool : kpool;
-        uint4 rows[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int s = sm.slot[4 * qd + r];
-          rows[r] = s >= 0 ? *reinterpret_cast<const uint4*>(base + ((int64_t)s * a.hkv + kvh) * D + 8 * c)
-                           : make_uint4(0, 0, 0, 0);
-        }
-        if (which == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&sm.k[(4 * qd + r) * KS + 8 * c]) = rows[r];
-        } else {
-          const int qk = qd & 3;
-          const int col = 16 * (qd >> 2) + 4 * (qk == 1 ? 2 : (qk == 2 ? 1 : qk));
-          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&rows[0]);
-          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&rows[1]);
-          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&rows[2]);
-          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&rows[3]);
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            uint2 lo2 = make_uint2((w0[p] & 0xffffu) | (w1[p] << 16), (w2[p] & 0xffffu) | (w3[p] << 16));
-            uint2 hi2 = make_uint2((w0[p] >> 16) | (w1[p] & 0xffff0000u), (w2[p] >> 16) | (w3[p] & 0xffff0000u));
-            *reinterpret_cast<uint2*>(&sm.vt[(8 * c + 2 * p) * VS + col]) = lo2;
-            *reinterpret_cast<uint2*>(&sm.vt[(8 * c + 2 * p + 1) * VS + col]) = hi2;
-          }
-        }
-      }
-      __syncthreads();
+    nblk += (job[2] - job[1] + 63) >> 6;
+  }
 
+  uint4 kr[4], vr[4];
+  auto load_kv = [&](const int4& s) {
+    const int sl[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t off = (int64_t)sl[r] * slot_stride + head_off;
+      kr[r] = (doK && sl[r] >= 0) ? *reinterpret_cast<const uint4*>(kpool + off) : make_uint4(0, 0, 0, 0);
+      vr[r] = (doV && sl[r] >= 0) ? *reinterpret_cast<const uint4*>(vpool + off) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_kv = [&](KVTile<D>& t) {
+    if (doK) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&t.k[(4 * qd + r) * KS + 8 * cc]) = kr[r];
+    }
+    if (doV) {
+      const int qk = qd & 3;
+      const int col = 16 * (qd >> 2) + 4 * (qk == 1 ? 2 : (qk == 2 ? 1 : qk));
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint2 lo2 = make_uint2((w0[p] & 0xffffu) | (w1[p] << 16), (w2[p] & 0xffffu) | (w3[p] << 16));
+        const uint2 hi2 = make_uint2((w0[p] >> 16) | (w1[p] & 0xffff0000u), (w2[p] >> 16) | (w3[p] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&t.vt[(8 * cc + 2 * p) * VS + col]) = lo2;
+        *reinterpret_cast<uint2*>(&t.vt[(8 * cc + 2 * p + 1) * VS + col]) = hi2;
+      }
+    }
+  };
+
+  if (nblk > 0) {
+    // ---- prologue: block 0 into LDS, slots of block 1 in flight ----
+    BlockIter it_slot, it_comp;
+    iter_job(a, it_slot, jb);
+    it_comp = it_slot;
+    int4 slots_next = load_slots(it_slot, qd);
+    iter_next(a, it_slot, je);
+    load_kv(slots_next);
+    if (nblk > 1) {
+      slots_next = load_slots(it_slot, qd);
+      iter_next(a, it_slot, je);
+    }
+    store_kv(buf[0]);
+    __syncthreads();
+
+    int cur_job = -1, lim = 0;
+    bool wave_job = false;
+    for (int b = 0; b < nblk; ++b) {
+      // ---- issue the loads of block b+1 and the slot reads of block b+2 ----
+      if (b + 1 < nblk) load_kv(slots_next);
+      int4 slots_after = slots_next;
+      if (b + 2 < nblk) {
+        slots_after = load_slots(it_slot, qd);
+        iter_next(a, it_slot, je);
+      }
+      // ---- compute block b ----
+      if (it_comp.j != cur_job) {
+        cur_job = it_comp.j;
+        const int32_t* job = a.jobs + (int64_t)cur_job * kJobWords;
+        const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+        lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+        wave_job = wave_live && __ballot(lim > job[1]) != 0;
+      }
+      const KVTile<D>& t = buf[b & 1];
       if (wave_job) {
-        // ---- S^T = K Q^T for 64 keys x this wave's 32 queries ----
+        // S^T = K Q^T for 64 keys x this wave's 32 queries
         f32x16 s[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          s[b] = f32x16{};
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          s[kb2] = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < KSTEPS; ++ks) {
-            bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.k[(32 * b + li) * KS + 16 * ks + 8 * hi]);
-            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[b], 0, 0, 0);
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t.k[(32 * kb2 + li) * KS + 16 * ks + 8 * hi]);
+            s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb2], 0, 0, 0);
           }
         }
-        // ---- mask + online softmax (base 2) ----
-        const int rel = lim - kb;  // keys with local index < rel are visible
+        // mask (only where some lane of the wave needs it) + online softmax, base 2
+        const int rel = lim - it_comp.kb;  // keys with local index < rel are visible
+        if (__ballot(rel < 64)) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kl = 32 * kb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
+              s[kb2][r] = kl < rel ? s[kb2][r] : -INFINITY;
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int kl = 32 * b + 8 * (r >> 2) + 4 * hi + (r & 3);
-            float v = kl < rel ? s[b][r] : -INFINITY;
-            s[b][r] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx * c2);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2_fast(m_run - m_use);
         float lsum = 0.f;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float p = exp2_fast(fmaf(s[b][r], c2, -m_use));
-            s[b][r] = p;
+            const float p = exp2_fast(fmaf(s[kb2][r], c2, -m_use));
+            s[kb2][r] = p;
             lsum += p;
           }
         l_run = l_run * alpha + lsum;
         m_run = m_new;
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
-          for (int b = 0; b < DB; ++b)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
         }
-        // ---- P (B operand): 16-key step ks uses registers 8t..8t+7 of block ks/2 ----
+        // P (B operand): 16-key step ks uses registers 8t..8t+7 of block ks/2
         bf16x8 pk[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
-        // ---- O^T += V^T P^T ----
+        // O^T += V^T P^T
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 va = *reinterpret_cast<const bf16x8*>(&sm.vt[(32 * b + li) * VS + 16 * ks + 8 * hi]);
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], acc[b], 0, 0, 0);
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(&t.vt[(32 * db + li) * VS + 16 * ks + 8 * hi]);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], acc[db], 0, 0, 0);
           }
       }
+      // ---- block b+1 into the other buffer ----
+      if (b + 1 < nblk) store_kv(buf[(b + 1) & 1]);
+      slots_next = slots_after;
+      iter_next(a, it_comp, je);
       __syncthreads();
     }
   }
@@ -307,15 +372,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
       __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
 #pragma unroll
-      for (int b = 0; b < DB; ++b)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int d = 32 * b + 8 * g4 + 4 * hi;
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           bf16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[b][4 * g4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(dst + d) = v;
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hi) = v;
         }
     }
     return;
@@ -325,19 +388,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
     float* dst = a.ws_o + w * D;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * b + 8 * g4 + 4 * hi;
-        *reinterpret_cast<float4*>(dst + d) =
-            make_float4(acc[b][4 * g4] * inv, acc[b][4 * g4 + 1] * inv, acc[b][4 * g4 + 2] * inv, acc[b][4 * g4 + 3] * inv);
-      }
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g4 + 4 * hi) =
+            make_float4(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv, acc[db][4 * g4 + 2] * inv,
+                        acc[db][4 * g4 + 3] * inv);
     if (hi == 0) {
       a.ws_ml[w * 2] = m_run;
       a.ws_ml[w * 2 + 1] = l_tot;
     }
   }
-  arrive_and_merge<__bf16, D>(a, tile, kvh, &sm.flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -346,64 +407,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
-  __shared__ int s_flag;
   const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
   const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
   const int kvh = item[1];
   const int group = a.group;
   const int n_rows = tile[1] * group;
   const int row = threadIdx.x;
-  const bool row_ok = row < n_rows;
-  const int tloc = row_ok ? row / group : 0;
+  if (row >= n_rows) return;
+  const int tloc = row / group;
   float q[D], acc[D];
   float m_run = -INFINITY, l_run = 0.f;
-  int qpos = 0;
-  if (row_ok) {
-    const int32_t* tk = a.toks + (int64_t)(tile[0] + tloc) * kTokWords;
-    qpos = tk[1];
-    const float* src = reinterpret_cast<const float*>(a.q) + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D;
-    for (int d = 0; d < D; ++d) {
-      q[d] = src[d];
-      acc[d] = 0.f;
-    }
-    const float* kpool = reinterpret_cast<const float*>(a.kp);
-    const float* vpool = reinterpret_cast<const float*>(a.vp);
-    for (int j = item[2]; j < item[3]; ++j) {
-      const int32_t* job = a.jobs + (int64_t)j * kJobWords;
-      if (tloc < job[3] || tloc >= job[4]) continue;
-      const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
-      const int end = job[5] ? min(job[2], qpos + 1) : job[2];
-      for (int p = job[1]; p < end; ++p) {
-        const int64_t off = ((int64_t)prow[p] * a.hkv + kvh) * D;
-        float s = 0.f;
-        for (int d = 0; d < D; ++d) s = fmaf(q[d], kpool[off + d], s);
-        const float t = s * a.scale_log2;
-        const float m_new = fmaxf(m_run, t);
-        const float alpha = exp2f(m_run - m_new);
-        const float pw = exp2f(t - m_new);
-        l_run = l_run * alpha + pw;
-        for (int d = 0; d < D; ++d) acc[d] = fmaf(pw, vpool[off + d], acc[d] * alpha);
-        m_run = m_new;
-      }
+  const int32_t* tk = a.toks + (int64_t)(tile[0] + tloc) * kTokWords;
+  const int qpos = tk[1];
+  const float* src = reinterpret_cast<const float*>(a.q) + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D;
+  for (int d = 0; d < D; ++d) {
+    q[d] = src[d];
+    acc[d] = 0.f;
+  }
+  const float* kpool = reinterpret_cast<const float*>(a.kp);
+  const float* vpool = reinterpret_cast<const float*>(a.vp);
+  for (int j = item[2]; j < item[3]; ++j) {
+    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+    if (tloc < job[3] || tloc >= job[4]) continue;
+    const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
+    const int end = job[5] ? min(job[2], qpos + 1) : job[2];
+    for (int p = job[1]; p < end; ++p) {
+      const int64_t off = ((int64_t)prow[p] * a.hkv + kvh) * D;
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s = fmaf(q[d], kpool[off + d], s);
+      const float t = s * a.scale_log2;
+      const float m_new = fmaxf(m_run, t);
+      const float alpha = exp2f(m_run - m_new);
+      const float pw = exp2f(t - m_new);
+      l_run = l_run * alpha + pw;
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(pw, vpool[off + d], acc[d] * alpha);
+      m_run = m_new;
     }
   }
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   if (tile[4] < 0) {
-    if (row_ok) {
-      const int32_t q_index = a.toks[(int64_t)(tile[0] + tloc) * kTokWords];
-      float* dst = reinterpret_cast<float*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
-      for (int d = 0; d < D; ++d) dst[d] = acc[d] * inv;
-    }
+    float* dst = reinterpret_cast<float*>(a.o) + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D;
+    for (int d = 0; d < D; ++d) dst[d] = acc[d] * inv;
     return;
   }
   const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
-  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
+  if (tloc >= cr[0] && tloc < cr[1]) {
     const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
     for (int d = 0; d < D; ++d) a.ws_o[w * D + d] = acc[d] * inv;
     a.ws_ml[w * 2] = m_run;
     a.ws_ml[w * 2 + 1] = l_run;
   }
-  arrive_and_merge<float, D>(a, tile, kvh, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -444,32 +497,45 @@ struct Timing {
   int32_t used = 0;
 } g_timing;
 
-template <typename K>
-hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t st, int32_t kind, const AttnArgs& a) {
+// Launches the attention kernel and, for plans with split tiles, the merge
+// kernel behind it.  While timing is on, the first kernel carries the start
+// event and the last one the stop event (events bound to the dispatches).
+template <typename KA, typename KM>
+hipError_t launch(KA attn, KM merge, int64_t n_items, int64_t n_merge, hipStream_t st, int32_t kind,
+                  const AttnArgs& a) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
   if (g_timing.on && g_timing.used < g_timing.cap) {
-    int32_t i = g_timing.used;
+    const int32_t i = g_timing.used;
     while ((int32_t)g_timing.start.size() <= i) {
-      hipEvent_t e0, e1;
-      hipError_t e = hipEventCreate(&e0);
+      hipEvent_t x, y;
+      hipError_t e = hipEventCreate(&x);
       if (e != hipSuccess) return e;
-      e = hipEventCreate(&e1);
+      e = hipEventCreate(&y);
       if (e != hipSuccess) return e;
-      g_timing.start.push_back(e0);
-      g_timing.stop.push_back(e1);
+      g_timing.start.push_back(x);
+      g_timing.stop.push_back(y);
       g_timing.kind.push_back(0);
     }
     g_timing.kind[i] = kind;
     g_timing.used++;
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_timing.start[i], g_timing.stop[i], 0, a);
-  } else {
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+    e0 = g_timing.start[i];
+    e1 = g_timing.stop[i];
   }
+  const dim3 block(kThreads);
+  if (e0)
+    hipExtLaunchKernelGGL(attn, dim3((unsigned)n_items), block, 0, st, e0, n_merge ? nullptr : e1, 0, a);
+  else
+    hipLaunchKernelGGL(attn, dim3((unsigned)n_items), block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_merge == 0) return e;
+  if (e1)
+    hipExtLaunchKernelGGL(merge, dim3((unsigned)n_merge), block, 0, st, nullptr, e1, 0, a);
+  else
+    hipLaunchKernelGGL(merge, dim3((unsigned)n_merge), block, 0, st, a);
   return hipGetLastError();
 }
 
-int hip_fail(hipError_t e, const char* what) {
-  return fail(RDX_EDEVICE, "%s: %s", what, hipGetErrorString(e));
-}
+int hip_fail(hipError_t e, const char* what) { return fail(RDX_EDEVICE, "%s: %s", what, hipGetErrorString(e)); }
 
 bool same_shape(const rdx_attn_desc& a, const rdx_attn_desc& b) {
   return a.dtype == b.dtype && a.num_q_heads == b.num_q_heads && a.num_kv_heads == b.num_kv_heads &&
@@ -491,7 +557,8 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   if (!dev_plan || !q || !kp || !vp || !pt || !o) return fail(RDX_EINVAL, "attention: null device pointer");
   if (p->ws_bytes > 0 && (!ws || ws_bytes < p->ws_bytes))
     return fail(RDX_EINVAL, "attention: workspace of %lld bytes needed", (long long)p->ws_bytes);
-  if (n_items > INT32_MAX) return fail(RDX_EINVAL, "attention: too many work items");
+  const int64_t n_merge = p->num_split_tiles * desc->num_kv_heads;
+  if (n_items > INT32_MAX || n_merge > INT32_MAX) return fail(RDX_EINVAL, "attention: too many work items");
   const int32_t* base = reinterpret_cast<const int32_t*>(dev_plan);
   AttnArgs a;
   a.items = base + p->off_items;
@@ -499,6 +566,7 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   a.jobs = base + p->off_jobs;
   a.toks = base + p->off_toks;
   a.contribs = base + p->off_contribs;
+  a.splits = base + p->off_splits;
   a.page_table = pt;
   a.ld = p->ld;
   a.q = q;
@@ -506,8 +574,7 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   a.vp = vp;
   a.o = o;
   char* wsb = reinterpret_cast<char*>(ws);
-  a.counters = reinterpret_cast<int32_t*>(wsb);
-  a.ws_o = wsb ? reinterpret_cast<float*>(wsb + p->ws_o_offset) : nullptr;
+  a.ws_o = reinterpret_cast<float*>(wsb);
   a.ws_ml = wsb ? reinterpret_cast<float*>(wsb + p->ws_ml_offset) : nullptr;
   a.ws_tokens = p->ws_tokens;
   a.hq = desc->num_q_heads;
@@ -516,14 +583,14 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   const float scale = desc->sm_scale > 0.f ? desc->sm_scale : 1.f / sqrtf((float)desc->head_dim);
   a.scale_log2 = scale * kLog2e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)n_items), block(kThreads);
   hipError_t e;
   if (desc->dtype == RDX_BF16)
-    e = desc->head_dim == 128 ? launch(attn_bf16_kernel<128>, grid, block, st, kind, a)
-                              : launch(attn_bf16_kernel<64>, grid, block, st, kind, a);
+    e = desc->head_dim == 128
+            ? launch(attn_bf16_kernel<128>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a)
+            : launch(attn_bf16_kernel<64>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a);
   else
-    e = desc->head_dim == 128 ? launch(attn_f32_kernel<128>, grid, block, st, kind, a)
-                              : launch(attn_f32_kernel<64>, grid, block, st, kind, a);
+    e = desc->head_dim == 128 ? launch(attn_f32_kernel<128>, merge_kernel<float, 128>, n_items, n_merge, st, kind, a)
+                              : launch(attn_f32_kernel<64>, merge_kernel<float, 64>, n_items, n_merge, st, kind, a);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -581,7 +648,7 @@ int rdx_plan_upload(rdx_plan* hplan, void* dev_plan, int64_t dev_plan_bytes, int
     if (p->pinned) hipHostFree(p->pinned);
     p->pinned = nullptr;
     p->pinned_bytes = 0;
-    int64_t want = bytes + bytes / 2 + 4096;
+    const int64_t want = bytes + bytes / 2 + 4096;
     e = hipHostMalloc(&p->pinned, want, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
     p->pinned_bytes = want;
@@ -598,6 +665,7 @@ int rdx_plan_upload(rdx_plan* hplan, void* dev_plan, int64_t dev_plan_bytes, int
   put(p->off_runs, p->runs);
   put(p->off_run_slots, p->run_slots);
   put(p->off_new, p->new_slots);
+  put(p->off_splits, p->splits);
   e = hipMemcpyAsync(dev_plan, p->pinned, bytes, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
   if (n_runs > 0) {

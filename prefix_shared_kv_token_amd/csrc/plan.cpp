@@ -17,8 +17,8 @@
 //
 // Items.  When the launch would have too few (tile, KV head) pairs to fill
 // the GPU, the key ranges of a tile are cut into chunks run as separate work
-// items; each writes a partial softmax state and the last to finish merges
-// them (log-sum-exp) in the same launch.
+// items; each writes a partial softmax state, and a merge pass right after
+// combines them by log-sum-exp.
 #include "plan.h"
 
 #include <algorithm>
@@ -208,7 +208,9 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
 
   // ---- split into items ----
   const int hkv = desc.num_kv_heads;
-  int64_t target = target_items > 0 ? target_items : 1024;
+  // default launch size the split aims for: extend only splits when fewer
+  // than ~one round of workgroups (2 per CU) exists; decode aims for 4 per CU
+  int64_t target = target_items > 0 ? target_items : (kind == RDX_PLAN_EXTEND ? 512 : 1024);
   int64_t chunk = INT64_MAX;
   if ((int64_t)ntiles * hkv < target && total_cost > 0) {
     int64_t per_kvh = std::max<int64_t>(1, target / hkv);
@@ -218,6 +220,7 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   jobs.clear();
   contribs.clear();
   items.clear();
+  splits.clear();
   num_split_tiles = 0;
   ws_tokens = 0;
   key_rows = 0;
@@ -247,6 +250,7 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     tl[2] = (int32_t)mine.size();
     tl[3] = (int32_t)(contribs.size() / kContribWords);
     if (mine.size() > 1) {
+      splits.push_back(t);
       tl[4] = (int32_t)num_split_tiles++;
       for (auto& it : mine) {
         int32_t lo = INT32_MAX, hi = 0;
@@ -271,9 +275,8 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
 
   // ---- workspace ----
   const int64_t hq = desc.num_q_heads, d = desc.head_dim;
-  ws_counter_bytes = ((num_split_tiles * hkv * 4) + 255) / 256 * 256;
-  ws_o_offset = ws_counter_bytes;
-  ws_ml_offset = ws_o_offset + (ws_tokens * hq * d * 4 + 255) / 256 * 256;
+  // partial outputs [kvh][ws_token][grouped head][D] fp32, then (m, l) pairs
+  ws_ml_offset = (ws_tokens * hq * d * 4 + 255) / 256 * 256;
   ws_bytes = num_split_tiles ? ws_ml_offset + ws_tokens * hq * 2 * 4 : 0;
   layout();
   built = true;
@@ -290,6 +293,7 @@ void Plan::layout() {
   off_runs = w; w = align16(w + (int64_t)runs.size());
   off_run_slots = w; w = align16(w + (int64_t)run_slots.size());
   off_new = w; w = align16(w + (int64_t)new_slots.size());
+  off_splits = w; w = align16(w + (int64_t)splits.size());
   total_words = std::max<int64_t>(w, 16);
 }
 

@@ -44,6 +44,8 @@ class Runtime:
 
         self.torch = torch
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.desc = rdx.attn_desc(rdx.BF16 if dtype == "bf16" else rdx.F32, num_q_heads, num_kv_heads,
@@ -78,8 +80,7 @@ class Runtime:
 
     def _workspace(self, nbytes: int):
         if self.workspace.numel() < nbytes:
-            # counters must start at zero; every launch returns them to zero
-            self.workspace = self.torch.zeros(max(nbytes, 2 * self.workspace.numel()), dtype=self.torch.uint8,
+            self.workspace = self.torch.empty(max(nbytes, 2 * self.workspace.numel()), dtype=self.torch.uint8,
                                               device=self.device)
         return self.workspace
 
