@@ -36,7 +36,9 @@ struct AttnArgs {
   const int32_t* jobs;
   const int32_t* toks;
   const int32_t* contribs;
-  const int32_t* splits;
+  const int32_t* cptr;
+  const int32_t* clist;
+  const int32_t* mblocks;
   const int32_t* page_table;
   int64_t ld;
   const void* q;
@@ -60,51 +62,56 @@ __device__ __forceinline__ void store_out(__bf16* p, float v) { *p = (__bf16)v; 
 // head hh) lives at
 //   ws_o [((kvh * ws_tokens + base + t - lo) * group + hh) * D + d]
 //   ws_ml[((kvh * ws_tokens + base + t - lo) * group + hh) * 2 + {0: m, 1: l}]
-// with o already normalised by its own l.  One workgroup per (split tile,
-// KV head); it runs after the attention kernel in stream order.
+// with o already normalised by its own l.  Each workgroup merges 16 query
+// rows of one split tile for one KV head (16 lanes per row, D/16 values per
+// lane), visiting only the contributions that cover the row's token.  It
+// runs after the attention kernel in stream order.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
-  const int32_t* tile = a.tiles + (int64_t)a.splits[blockIdx.x / a.hkv] * kTileWords;
+  constexpr int kPer = D / 16;  // values per lane
+  const int32_t* mb = a.mblocks + (int64_t)(blockIdx.x / a.hkv) * 2;
   const int kvh = blockIdx.x % a.hkv;
-  const int n_tok = tile[1], n_contrib = tile[2], cbeg = tile[3];
+  const int32_t* tile = a.tiles + (int64_t)mb[0] * kTileWords;
   const int group = a.group;
-  const int n_rows = n_tok * group;
-  T* out = reinterpret_cast<T*>(a.o);
-  constexpr int kVec = 4;
-  constexpr int kPer = D / kVec;  // float4 columns per row
-  for (int idx = threadIdx.x; idx < n_rows * kPer; idx += kThreads) {
-    const int row = idx / kPer, col = (idx % kPer) * kVec;
-    const int t = row / group, hh = row % group;
-    float mmax = -INFINITY;
-    for (int c = 0; c < n_contrib; ++c) {
-      const int32_t* cr = a.contribs + (int64_t)(cbeg + c) * kContribWords;
-      if (t < cr[0] || t >= cr[1]) continue;
-      const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
-      mmax = fmaxf(mmax, a.ws_ml[w * 2]);
-    }
-    float acc[kVec] = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    for (int c = 0; c < n_contrib; ++c) {
-      const int32_t* cr = a.contribs + (int64_t)(cbeg + c) * kContribWords;
-      if (t < cr[0] || t >= cr[1]) continue;
-      const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
-      const float l = a.ws_ml[w * 2 + 1];
-      if (l <= 0.f) continue;
-      const float wt = l * exp2_fast(a.ws_ml[w * 2] - mmax);
-      const float4 v = *reinterpret_cast<const float4*>(a.ws_o + w * D + col);
-      acc[0] += wt * v.x;
-      acc[1] += wt * v.y;
-      acc[2] += wt * v.z;
-      acc[3] += wt * v.w;
-      wsum += wt;
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const int32_t q_index = a.toks[(int64_t)(tile[0] + t) * kTokWords];
-    T* dst = out + ((int64_t)q_index * a.hq + (int64_t)kvh * group + hh) * D + col;
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) store_out(dst + e, acc[e] * inv);
+  const int row = mb[1] + threadIdx.x / 16;
+  if (row >= tile[1] * group) return;
+  const int part = threadIdx.x % 16;
+  const int t = row / group, hh = row % group;
+  const int32_t* cp = a.cptr + tile[5] + t;
+  const int cs = cp[0], ce = cp[1];
+  float mmax = -INFINITY;
+  for (int k = cs; k < ce; ++k) {
+    const int32_t* cr = a.contribs + (int64_t)(tile[3] + a.clist[k]) * kContribWords;
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
+    mmax = fmaxf(mmax, a.ws_ml[w * 2]);
   }
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  for (int k = cs; k < ce; ++k) {
+    const int32_t* cr = a.contribs + (int64_t)(tile[3] + a.clist[k]) * kContribWords;
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
+    const float l = a.ws_ml[w * 2 + 1];
+    if (l <= 0.f) continue;
+    const float wt = l * exp2_fast(a.ws_ml[w * 2] - mmax);
+    const float4* src = reinterpret_cast<const float4*>(a.ws_o + w * D + part * kPer);
+#pragma unroll
+    for (int e = 0; e < kPer / 4; ++e) {
+      const float4 v = src[e];
+      acc[4 * e] += wt * v.x;
+      acc[4 * e + 1] += wt * v.y;
+      acc[4 * e + 2] += wt * v.z;
+      acc[4 * e + 3] += wt * v.w;
+    }
+    wsum += wt;
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int32_t q_index = a.toks[(int64_t)(tile[0] + t) * kTokWords];
+  T* dst = reinterpret_cast<T*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + hh) * D + part * kPer;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_out(dst + e, acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -128,15 +135,69 @@ __device__ __forceinline__ void iter_next(const AttnArgs& a, BlockIter& it, int 
   if (it.kb >= it.k1 && it.j + 1 < je) iter_job(a, it, it.j + 1);
 }
 
-// slots of keys 4qd .. 4qd+3 of the block (-1 past the job's end)
+// Slots of keys 4qd .. 4qd+3 of the block.  Branch-free: positions past the
+// job's end read the job's last position instead (a valid slot); those keys
+// are masked out of the softmax, so their K/V rows only cost bandwidth.
 __device__ __forceinline__ int4 load_slots(const BlockIter& it, int qd) {
-  const int p = it.kb + 4 * qd;
+  const int p = it.kb + 4 * qd, last = it.k1 - 1;
   int4 s;
-  s.x = p < it.k1 ? it.prow[p] : -1;
-  s.y = p + 1 < it.k1 ? it.prow[p + 1] : -1;
-  s.z = p + 2 < it.k1 ? it.prow[p + 2] : -1;
-  s.w = p + 3 < it.k1 ? it.prow[p + 3] : -1;
+  s.x = it.prow[min(p, last)];
+  s.y = it.prow[min(p + 1, last)];
+  s.z = it.prow[min(p + 2, last)];
+  s.w = it.prow[min(p + 3, last)];
   return s;
+}
+
+// ---------------------------------------------------------------------------
+// K/V tile staging helpers (4 key rows x one 16-byte chunk per unit)
+// ---------------------------------------------------------------------------
+struct Rows4 {
+  uint4 a, b, c, d;
+};
+
+__device__ __forceinline__ Rows4 load_rows(const __bf16* pool, const int4& s, int64_t stride, int64_t off) {
+  Rows4 r;
+  r.a = *reinterpret_cast<const uint4*>(pool + (int64_t)s.x * stride + off);
+  r.b = *reinterpret_cast<const uint4*>(pool + (int64_t)s.y * stride + off);
+  r.c = *reinterpret_cast<const uint4*>(pool + (int64_t)s.z * stride + off);
+  r.d = *reinterpret_cast<const uint4*>(pool + (int64_t)s.w * stride + off);
+  return r;
+}
+
+template <int D>
+__device__ __forceinline__ void store_k_rows(__bf16* k, const Rows4& r, int qd, int cc) {
+  constexpr int KS = D + 8;
+  __bf16* p = k + (4 * qd) * KS + 8 * cc;
+  *reinterpret_cast<uint4*>(p) = r.a;
+  *reinterpret_cast<uint4*>(p + KS) = r.b;
+  *reinterpret_cast<uint4*>(p + 2 * KS) = r.c;
+  *reinterpret_cast<uint4*>(p + 3 * KS) = r.d;
+}
+
+// V^T column of key quad qd: quads are stored in the MFMA contraction order
+// (within each 16 keys: quads 0, 2, 1, 3)
+__device__ __forceinline__ int vt_col(int qd) {
+  const int qk = qd & 3;
+  return 16 * (qd >> 2) + 4 * (qk == 1 ? 2 : (qk == 2 ? 1 : qk));
+}
+
+// 4 keys x 8 d of V -> 8 rows (d = 8 cc ..) x 4 keys of V^T
+__device__ __forceinline__ void vt_pair(__bf16* vt, int vs, int d, int col, uint32_t w0, uint32_t w1, uint32_t w2,
+                                        uint32_t w3) {
+  const uint2 lo2 = make_uint2((w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16));
+  const uint2 hi2 = make_uint2((w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u));
+  *reinterpret_cast<uint2*>(vt + d * vs + col) = lo2;
+  *reinterpret_cast<uint2*>(vt + (d + 1) * vs + col) = hi2;
+}
+
+template <int D>
+__device__ __forceinline__ void store_vt_rows(__bf16* vt, const Rows4& r, int cc, int col) {
+  constexpr int VS = 64 + 8;
+  const int d = 8 * cc;
+  vt_pair(vt, VS, d, col, r.a.x, r.b.x, r.c.x, r.d.x);
+  vt_pair(vt, VS, d + 2, col, r.a.y, r.b.y, r.c.y, r.d.y);
+  vt_pair(vt, VS, d + 4, col, r.a.z, r.b.z, r.c.z, r.d.z);
+  vt_pair(vt, VS, d + 6, col, r.a.w, r.b.w, r.c.w, r.d.w);
 }
 
 // ---------------------------------------------------------------------------
@@ -172,11 +233,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int UNITS = 16 * CH;  // (key quad, chunk) units per matrix
   constexpr bool BOTH = 2 * UNITS > kThreads;  // each thread loads K and V of one unit
 
+  // Load units: a unit is (key quad qd, 16-byte chunk cc) of the 64 x D tile.
+  // K units vary cc fastest (16 lanes read one contiguous key row; row-major
+  // LDS stores).  V units vary qd fastest so that 16 consecutive lanes store
+  // 16 different 8-byte key quads of one V^T row (no LDS bank conflicts).
+  // head_dim 128: every thread loads one K and one V unit; 64: threads
+  // 0..127 load K, 128..255 load V (wave-uniform).
   const int tid = threadIdx.x;
-  const int uu = BOTH ? tid : tid % UNITS;
   const bool doK = BOTH || tid < UNITS;
   const bool doV = BOTH || tid >= UNITS;
-  const int qd = uu / CH, cc = uu % CH;
+  const int uk = tid % UNITS;
+  const int uv = BOTH ? tid : tid - UNITS;
+  const int qd_k = uk / CH, cc_k = uk % CH;
+  const int qd_v = uv % 16, cc_v = uv / 16;
+  const int qd1 = doK ? qd_k : qd_v;  // the unit whose slots feed kr (head_dim 64: this thread's only unit)
 
   const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
   const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
@@ -217,8 +287,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
   const __bf16* kpool = reinterpret_cast<const __bf16*>(a.kp);
   const __bf16* vpool = reinterpret_cast<const __bf16*>(a.vp);
-  const int64_t head_off = (int64_t)kvh * D + 8 * cc;
   const int64_t slot_stride = (int64_t)a.hkv * D;
+  const int64_t head_off1 = (int64_t)kvh * D + 8 * (doK ? cc_k : cc_v);
+  const int64_t head_off2 = (int64_t)kvh * D + 8 * cc_v;
 
   int nblk = 0;
   for (int j = jb; j < je; ++j) {
@@ -226,35 +297,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     nblk += (job[2] - job[1] + 63) >> 6;
   }
 
-  uint4 kr[4], vr[4];
-  auto load_kv = [&](const int4& s) {
-    const int sl[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t off = (int64_t)sl[r] * slot_stride + head_off;
-      kr[r] = (doK && sl[r] >= 0) ? *reinterpret_cast<const uint4*>(kpool + off) : make_uint4(0, 0, 0, 0);
-      vr[r] = (doV && sl[r] >= 0) ? *reinterpret_cast<const uint4*>(vpool + off) : make_uint4(0, 0, 0, 0);
-    }
+  // r1: rows of the thread's first unit (K; head_dim 64: K or V, whichever
+  // this thread loads); r2: rows of its V unit (head_dim 128 only).
+  Rows4 r1, r2;
+  const __bf16* pool1 = doK ? kpool : vpool;
+  auto load_kv = [&](const int4& s1, const int4& s2) {
+    r1 = load_rows(pool1, s1, slot_stride, head_off1);
+    if constexpr (BOTH) r2 = load_rows(vpool, s2, slot_stride, head_off2);
   };
+  const int vcol = vt_col(qd_v);
   auto store_kv = [&](KVTile<D>& t) {
-    if (doK) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&t.k[(4 * qd + r) * KS + 8 * cc]) = kr[r];
-    }
-    if (doV) {
-      const int qk = qd & 3;
-      const int col = 16 * (qd >> 2) + 4 * (qk == 1 ? 2 : (qk == 2 ? 1 : qk));
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint2 lo2 = make_uint2((w0[p] & 0xffffu) | (w1[p] << 16), (w2[p] & 0xffffu) | (w3[p] << 16));
-        const uint2 hi2 = make_uint2((w0[p] >> 16) | (w1[p] & 0xffff0000u), (w2[p] >> 16) | (w3[p] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&t.vt[(8 * cc + 2 * p) * VS + col]) = lo2;
-        *reinterpret_cast<uint2*>(&t.vt[(8 * cc + 2 * p + 1) * VS + col]) = hi2;
-      }
+    if constexpr (BOTH) {
+      store_k_rows<D>(t.k, r1, qd_k, cc_k);
+      store_vt_rows<D>(t.vt, r2, cc_v, vcol);
+    } else if (doK) {
+      store_k_rows<D>(t.k, r1, qd_k, cc_k);
+    } else {
+      store_vt_rows<D>(t.vt, r1, cc_v, vcol);
     }
   };
 
@@ -263,11 +322,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     BlockIter it_slot, it_comp;
     iter_job(a, it_slot, jb);
     it_comp = it_slot;
-    int4 slots_next = load_slots(it_slot, qd);
+    int4 slots_next = load_slots(it_slot, qd1);
+    int4 slots_next2 = BOTH ? load_slots(it_slot, qd_v) : slots_next;
     iter_next(a, it_slot, je);
-    load_kv(slots_next);
+    load_kv(slots_next, slots_next2);
     if (nblk > 1) {
-      slots_next = load_slots(it_slot, qd);
+      slots_next = load_slots(it_slot, qd1);
+      if (BOTH) slots_next2 = load_slots(it_slot, qd_v);
       iter_next(a, it_slot, je);
     }
     store_kv(buf[0]);
@@ -277,10 +338,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     bool wave_job = false;
     for (int b = 0; b < nblk; ++b) {
       // ---- issue the loads of block b+1 and the slot reads of block b+2 ----
-      if (b + 1 < nblk) load_kv(slots_next);
-      int4 slots_after = slots_next;
+      if (b + 1 < nblk) load_kv(slots_next, slots_next2);
+      int4 slots_after = slots_next, slots_after2 = slots_next2;
       if (b + 2 < nblk) {
-        slots_after = load_slots(it_slot, qd);
+        slots_after = load_slots(it_slot, qd1);
+        if (BOTH) slots_after2 = load_slots(it_slot, qd_v);
         iter_next(a, it_slot, je);
       }
       // ---- compute block b ----
@@ -321,7 +383,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * c2);
+        // Lazy rescale: the running max moves only when a score exceeds it by
+        // more than 2^8, so probabilities stay <= 256 (exact: the same stale
+        // max scales numerator and denominator) and most blocks skip the
+        // O rescale.
+        const float t_max = mx * c2;
+        const float m_new = t_max > m_run + 8.f ? t_max : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2_fast(m_run - m_use);
         float lsum = 0.f;
@@ -359,6 +426,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       // ---- block b+1 into the other buffer ----
       if (b + 1 < nblk) store_kv(buf[(b + 1) & 1]);
       slots_next = slots_after;
+      slots_next2 = slots_after2;
       iter_next(a, it_comp, je);
       __syncthreads();
     }
@@ -557,7 +625,7 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   if (!dev_plan || !q || !kp || !vp || !pt || !o) return fail(RDX_EINVAL, "attention: null device pointer");
   if (p->ws_bytes > 0 && (!ws || ws_bytes < p->ws_bytes))
     return fail(RDX_EINVAL, "attention: workspace of %lld bytes needed", (long long)p->ws_bytes);
-  const int64_t n_merge = p->num_split_tiles * desc->num_kv_heads;
+  const int64_t n_merge = (int64_t)(p->mblocks.size() / 2) * desc->num_kv_heads;
   if (n_items > INT32_MAX || n_merge > INT32_MAX) return fail(RDX_EINVAL, "attention: too many work items");
   const int32_t* base = reinterpret_cast<const int32_t*>(dev_plan);
   AttnArgs a;
@@ -566,7 +634,9 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   a.jobs = base + p->off_jobs;
   a.toks = base + p->off_toks;
   a.contribs = base + p->off_contribs;
-  a.splits = base + p->off_splits;
+  a.cptr = base + p->off_cptr;
+  a.clist = base + p->off_clist;
+  a.mblocks = base + p->off_mblocks;
   a.page_table = pt;
   a.ld = p->ld;
   a.q = q;
@@ -665,7 +735,9 @@ int rdx_plan_upload(rdx_plan* hplan, void* dev_plan, int64_t dev_plan_bytes, int
   put(p->off_runs, p->runs);
   put(p->off_run_slots, p->run_slots);
   put(p->off_new, p->new_slots);
-  put(p->off_splits, p->splits);
+  put(p->off_cptr, p->cptr);
+  put(p->off_clist, p->clist);
+  put(p->off_mblocks, p->mblocks);
   e = hipMemcpyAsync(dev_plan, p->pinned, bytes, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
   if (n_runs > 0) {

@@ -220,7 +220,9 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   jobs.clear();
   contribs.clear();
   items.clear();
-  splits.clear();
+  cptr.clear();
+  clist.clear();
+  mblocks.clear();
   num_split_tiles = 0;
   ws_tokens = 0;
   key_rows = 0;
@@ -250,8 +252,8 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     tl[2] = (int32_t)mine.size();
     tl[3] = (int32_t)(contribs.size() / kContribWords);
     if (mine.size() > 1) {
-      splits.push_back(t);
       tl[4] = (int32_t)num_split_tiles++;
+      const int cbase = (int)(contribs.size() / kContribWords);
       for (auto& it : mine) {
         int32_t lo = INT32_MAX, hi = 0;
         for (int32_t jj = it.jb; jj < it.je; ++jj) {
@@ -261,6 +263,18 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
         contribs.insert(contribs.end(), {lo, hi, (int32_t)ws_tokens, 0});
         ws_tokens += hi - lo;
       }
+      tl = &tiles[t * kTileWords];
+      tl[5] = (int32_t)cptr.size();
+      for (int tok = 0; tok < tl[1]; ++tok) {
+        cptr.push_back((int32_t)clist.size());
+        for (int c = 0; c < (int)mine.size(); ++c) {
+          const int32_t* cr = &contribs[(cbase + c) * kContribWords];
+          if (tok >= cr[0] && tok < cr[1]) clist.push_back(c);
+        }
+      }
+      cptr.push_back((int32_t)clist.size());
+      const int rows = tl[1] * group();
+      for (int r0 = 0; r0 < rows; r0 += kMergeRows) mblocks.insert(mblocks.end(), {t, r0});
     }
     for (auto& it : mine) {
       its.push_back(it);
@@ -293,7 +307,9 @@ void Plan::layout() {
   off_runs = w; w = align16(w + (int64_t)runs.size());
   off_run_slots = w; w = align16(w + (int64_t)run_slots.size());
   off_new = w; w = align16(w + (int64_t)new_slots.size());
-  off_splits = w; w = align16(w + (int64_t)splits.size());
+  off_cptr = w; w = align16(w + (int64_t)cptr.size());
+  off_clist = w; w = align16(w + (int64_t)clist.size());
+  off_mblocks = w; w = align16(w + (int64_t)mblocks.size());
   total_words = std::max<int64_t>(w, 16);
 }
 

@@ -21,11 +21,12 @@ constexpr int kKeyBlock = 64;    // keys per inner iteration of the kernels
 
 // Record layouts (int32 words) -- shared with the device code.
 constexpr int kItemWords = 8;     // tile, kv_head, job_begin, job_end, contrib
-constexpr int kTileWords = 8;     // tok_begin, n_tok, n_contrib, contrib_begin, split index (-1: none)
+constexpr int kTileWords = 8;     // tok_begin, n_tok, n_contrib, contrib_begin, split index (-1: none), cptr base
 constexpr int kJobWords = 8;      // page_row, key_begin, key_end, tok_lo, tok_hi, causal
 constexpr int kTokWords = 2;      // q_index, position
 constexpr int kContribWords = 4;  // tok_lo, tok_hi, ws_token_base
 constexpr int kRunWords = 4;      // page_row, pos_begin, count, src_offset
+constexpr int kMergeRows = 16;    // query rows per merge workgroup (16 lanes per row)
 
 struct Plan {
   rdx_attn_desc desc{};
@@ -33,12 +34,16 @@ struct Plan {
   int32_t target_items = 0;
   int64_t ld = 0;
   // host records
-  std::vector<int32_t> items, tiles, jobs, toks, contribs, runs, run_slots, new_slots, splits;
+  // merge of split tiles: per tile token, the contributions covering it
+  // (cptr: n_tok + 1 offsets per split tile, tile word 5 = its base; clist:
+  // contribution indices local to the tile), and 16-row merge blocks
+  std::vector<int32_t> items, tiles, jobs, toks, contribs, runs, run_slots, new_slots, cptr, clist, mblocks;
   int64_t num_split_tiles = 0, num_shared_segments = 0, ws_tokens = 0, key_rows = 0;
   int64_t max_page_row = -1;
   // device blob layout, in int32 words
   int64_t off_items = 0, off_tiles = 0, off_jobs = 0, off_toks = 0, off_contribs = 0,
-          off_runs = 0, off_run_slots = 0, off_new = 0, off_splits = 0, total_words = 0;
+          off_runs = 0, off_run_slots = 0, off_new = 0, off_cptr = 0, off_clist = 0, off_mblocks = 0,
+          total_words = 0;
   int64_t ws_ml_offset = 0, ws_bytes = 0;
   bool built = false;
   // upload staging (pinned host memory + completion event), owned by the plan
