@@ -48,6 +48,7 @@ struct AttnArgs {
   float* ws_o;
   float* ws_ml;
   int64_t ws_tokens;
+  int64_t pool_bytes;  // bytes of each KV pool
   int hq, hkv, group;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -135,17 +136,11 @@ __device__ __forceinline__ void iter_next(const AttnArgs& a, BlockIter& it, int 
   if (it.kb >= it.k1 && it.j + 1 < je) iter_job(a, it, it.j + 1);
 }
 
-// Slots of keys 4qd .. 4qd+3 of the block.  Branch-free: positions past the
-// job's end read the job's last position instead (a valid slot); those keys
-// are masked out of the softmax, so their K/V rows only cost bandwidth.
-__device__ __forceinline__ int4 load_slots(const BlockIter& it, int qd) {
-  const int p = it.kb + 4 * qd, last = it.k1 - 1;
-  int4 s;
-  s.x = it.prow[min(p, last)];
-  s.y = it.prow[min(p + 1, last)];
-  s.z = it.prow[min(p + 2, last)];
-  s.w = it.prow[min(p + 3, last)];
-  return s;
+// Slot of key `i` of the block.  Positions past the job's end read the
+// job's last position instead (a valid slot); those keys are masked out of
+// the softmax, so their K/V rows only cost bandwidth.
+__device__ __forceinline__ int block_slot(const BlockIter& it, int i) {
+  return it.prow[min(it.kb + i, it.k1 - 1)];
 }
 
 // ---------------------------------------------------------------------------
@@ -155,14 +150,39 @@ struct Rows4 {
   uint4 a, b, c, d;
 };
 
-__device__ __forceinline__ Rows4 load_rows(const __bf16* pool, const int4& s, int64_t stride, int64_t off) {
-  Rows4 r;
-  r.a = *reinterpret_cast<const uint4*>(pool + (int64_t)s.x * stride + off);
-  r.b = *reinterpret_cast<const uint4*>(pool + (int64_t)s.y * stride + off);
-  r.c = *reinterpret_cast<const uint4*>(pool + (int64_t)s.z * stride + off);
-  r.d = *reinterpret_cast<const uint4*>(pool + (int64_t)s.w * stride + off);
-  return r;
-}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Reads 16-byte chunks of pool rows.  OFF32: the pool is under 4 GiB and is
+// addressed through a raw buffer resource with 32-bit byte offsets
+// (slot * row_bytes + chunk offset, a 24-bit multiply since such a pool has
+// fewer than 2^24 rows); otherwise 64-bit pointer arithmetic.
+template <bool OFF32>
+struct PoolReader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  const char* base;
+  uint32_t row_bytes;
+  __device__ void init(const void* pool, int64_t pool_bytes, uint32_t rb) {
+    base = reinterpret_cast<const char*>(pool);
+    row_bytes = rb;
+    if constexpr (OFF32) rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(pool), (short)0, (int)pool_bytes, 0x00020000);
+  }
+  __device__ __forceinline__ uint4 chunk(int slot, uint32_t off) const {
+    if constexpr (OFF32) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(__umul24((uint32_t)slot, row_bytes) + off), 0, 0);
+      return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+      return *reinterpret_cast<const uint4*>(base + (int64_t)slot * row_bytes + off);
+    }
+  }
+  __device__ __forceinline__ Rows4 rows(const int4& s, uint32_t off) const {
+    Rows4 r;
+    r.a = chunk(s.x, off);
+    r.b = chunk(s.y, off);
+    r.c = chunk(s.z, off);
+    r.d = chunk(s.w, off);
+    return r;
+  }
+};
 
 template <int D>
 __device__ __forceinline__ void store_k_rows(__bf16* k, const Rows4& r, int qd, int cc) {
@@ -184,8 +204,9 @@ __device__ __forceinline__ int vt_col(int qd) {
 // 4 keys x 8 d of V -> 8 rows (d = 8 cc ..) x 4 keys of V^T
 __device__ __forceinline__ void vt_pair(__bf16* vt, int vs, int d, int col, uint32_t w0, uint32_t w1, uint32_t w2,
                                         uint32_t w3) {
-  const uint2 lo2 = make_uint2((w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16));
-  const uint2 hi2 = make_uint2((w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u));
+  // low halves of (w0, w1) and (w2, w3) -> row d; high halves -> row d + 1
+  const uint2 lo2 = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u));
+  const uint2 hi2 = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u));
   *reinterpret_cast<uint2*>(vt + d * vs + col) = lo2;
   *reinterpret_cast<uint2*>(vt + (d + 1) * vs + col) = hi2;
 }
@@ -223,9 +244,10 @@ struct KVTile {
   __bf16 vt[D * VS];
 };
 
-template <int D>
+template <int D, bool OFF32>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ KVTile<D> buf[2];
+  __shared__ int4 slot_buf[2][16];  // page-table slots of the next two key blocks
   constexpr int KS = KVTile<D>::KS, VS = KVTile<D>::VS;
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over head_dim
   constexpr int DB = D / 32;      // 32-wide d blocks of the output
@@ -285,11 +307,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = a.scale_log2;
 
-  const __bf16* kpool = reinterpret_cast<const __bf16*>(a.kp);
-  const __bf16* vpool = reinterpret_cast<const __bf16*>(a.vp);
-  const int64_t slot_stride = (int64_t)a.hkv * D;
-  const int64_t head_off1 = (int64_t)kvh * D + 8 * (doK ? cc_k : cc_v);
-  const int64_t head_off2 = (int64_t)kvh * D + 8 * cc_v;
+  const uint32_t row_bytes = (uint32_t)(a.hkv * D * 2);
+  PoolReader<OFF32> kpool, vpool;
+  kpool.init(a.kp, a.pool_bytes, row_bytes);
+  vpool.init(a.vp, a.pool_bytes, row_bytes);
+  const uint32_t off1 = (uint32_t)(kvh * D + 8 * (doK ? cc_k : cc_v)) * 2;
+  const uint32_t off2 = (uint32_t)(kvh * D + 8 * cc_v) * 2;
 
   int nblk = 0;
   for (int j = jb; j < je; ++j) {
@@ -300,10 +323,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   // r1: rows of the thread's first unit (K; head_dim 64: K or V, whichever
   // this thread loads); r2: rows of its V unit (head_dim 128 only).
   Rows4 r1, r2;
-  const __bf16* pool1 = doK ? kpool : vpool;
-  auto load_kv = [&](const int4& s1, const int4& s2) {
-    r1 = load_rows(pool1, s1, slot_stride, head_off1);
-    if constexpr (BOTH) r2 = load_rows(vpool, s2, slot_stride, head_off2);
+  const PoolReader<OFF32>& pool1 = doK ? kpool : vpool;
+  auto load_kv = [&](const int4 (&sb)[16]) {
+    r1 = pool1.rows(sb[qd1], off1);
+    if constexpr (BOTH) r2 = vpool.rows(sb[qd_v], off2);
   };
   const int vcol = vt_col(qd_v);
   auto store_kv = [&](KVTile<D>& t) {
@@ -316,33 +339,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       store_vt_rows<D>(t.vt, r1, cc_v, vcol);
     }
   };
+  int* slot_words = reinterpret_cast<int*>(&slot_buf[0][0]);
 
   if (nblk > 0) {
-    // ---- prologue: block 0 into LDS, slots of block 1 in flight ----
+    // ---- prologue: slots of blocks 0 and 1 into LDS, block 0 into LDS ----
     BlockIter it_slot, it_comp;
     iter_job(a, it_slot, jb);
     it_comp = it_slot;
-    int4 slots_next = load_slots(it_slot, qd1);
-    int4 slots_next2 = BOTH ? load_slots(it_slot, qd_v) : slots_next;
+    if (tid < 64) slot_words[tid] = block_slot(it_slot, tid);
     iter_next(a, it_slot, je);
-    load_kv(slots_next, slots_next2);
     if (nblk > 1) {
-      slots_next = load_slots(it_slot, qd1);
-      if (BOTH) slots_next2 = load_slots(it_slot, qd_v);
+      if (tid < 64) slot_words[64 + tid] = block_slot(it_slot, tid);
       iter_next(a, it_slot, je);
     }
+    __syncthreads();
+    load_kv(slot_buf[0]);
     store_kv(buf[0]);
     __syncthreads();
 
     int cur_job = -1, lim = 0;
     bool wave_job = false;
     for (int b = 0; b < nblk; ++b) {
-      // ---- issue the loads of block b+1 and the slot reads of block b+2 ----
-      if (b + 1 < nblk) load_kv(slots_next, slots_next2);
-      int4 slots_after = slots_next, slots_after2 = slots_next2;
-      if (b + 2 < nblk) {
-        slots_after = load_slots(it_slot, qd1);
-        if (BOTH) slots_after2 = load_slots(it_slot, qd_v);
+      // ---- issue the K/V loads of block b+1 and the page-table read of block b+2 ----
+      if (b + 1 < nblk) load_kv(slot_buf[(b + 1) & 1]);
+      int slot_after = 0;
+      const bool more = b + 2 < nblk;
+      if (more) {
+        if (tid < 64) slot_after = block_slot(it_slot, tid);
         iter_next(a, it_slot, je);
       }
       // ---- compute block b ----
@@ -425,8 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       }
       // ---- block b+1 into the other buffer ----
       if (b + 1 < nblk) store_kv(buf[(b + 1) & 1]);
-      slots_next = slots_after;
-      slots_next2 = slots_after2;
+      if (more && tid < 64) slot_words[(b & 1) * 64 + tid] = slot_after;
       iter_next(a, it_comp, je);
       __syncthreads();
     }
@@ -647,6 +669,7 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   a.ws_o = reinterpret_cast<float*>(wsb);
   a.ws_ml = wsb ? reinterpret_cast<float*>(wsb + p->ws_ml_offset) : nullptr;
   a.ws_tokens = p->ws_tokens;
+  a.pool_bytes = desc->num_slots * desc->num_kv_heads * desc->head_dim * (desc->dtype == RDX_BF16 ? 2 : 4);
   a.hq = desc->num_q_heads;
   a.hkv = desc->num_kv_heads;
   a.group = a.hq / a.hkv;
@@ -654,10 +677,17 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   a.scale_log2 = scale * kLog2e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (desc->dtype == RDX_BF16)
-    e = desc->head_dim == 128
-            ? launch(attn_bf16_kernel<128>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a)
-            : launch(attn_bf16_kernel<64>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a);
+  // pools under 2 GiB are addressed with 32-bit buffer offsets (the buffer
+  // resource's record count is a signed 32-bit value here)
+  const bool off32 = a.pool_bytes < ((int64_t)1 << 31);
+  if (desc->dtype == RDX_BF16) {
+    if (desc->head_dim == 128)
+      e = off32 ? launch(attn_bf16_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a)
+                : launch(attn_bf16_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a);
+    else
+      e = off32 ? launch(attn_bf16_kernel<64, true>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a)
+                : launch(attn_bf16_kernel<64, false>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a);
+  }
   else
     e = desc->head_dim == 128 ? launch(attn_f32_kernel<128>, merge_kernel<float, 128>, n_items, n_merge, st, kind, a)
                               : launch(attn_f32_kernel<64>, merge_kernel<float, 64>, n_items, n_merge, st, kind, a);
