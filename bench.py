@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extend-items", type=int, default=0)
     ap.add_argument("--decode-items", type=int, default=0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU; multi-GPU runs are not part of it "
@@ -114,6 +116,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}))
+        return
 
     from prefix_shared_kv_token_amd import rdx
     from prefix_shared_kv_token_amd.driver import WorkloadRun

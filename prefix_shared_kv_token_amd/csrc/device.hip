@@ -76,38 +76,58 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
   const int32_t* tile = a.tiles + (int64_t)mb[0] * kTileWords;
   const int group = a.group;
   const int row = mb[1] + threadIdx.x / 16;
-  if (row >= tile[1] * group) return;
   const int part = threadIdx.x % 16;
-  const int t = row / group, hh = row % group;
+  const bool live = row < tile[1] * group;  // 16-lane groups stay whole for the shuffles
+  const int t = live ? row / group : 0, hh = live ? row % group : 0;
   const int32_t* cp = a.cptr + tile[5] + t;
-  const int cs = cp[0], ce = cp[1];
-  float mmax = -INFINITY;
-  for (int k = cs; k < ce; ++k) {
-    const int32_t* cr = a.contribs + (int64_t)(tile[3] + a.clist[k]) * kContribWords;
-    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
-    mmax = fmaxf(mmax, a.ws_ml[w * 2]);
-  }
+  const int cs = live ? cp[0] : 0, n = live ? cp[1] - cp[0] : 0;
+  const int rbase = kvh * (int)a.ws_tokens;
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
-  for (int k = cs; k < ce; ++k) {
-    const int32_t* cr = a.contribs + (int64_t)(tile[3] + a.clist[k]) * kContribWords;
-    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + t - cr[0]) * group + hh;
-    const float l = a.ws_ml[w * 2 + 1];
-    if (l <= 0.f) continue;
-    const float wt = l * exp2_fast(a.ws_ml[w * 2] - mmax);
-    const float4* src = reinterpret_cast<const float4*>(a.ws_o + w * D + part * kPer);
-#pragma unroll
-    for (int e = 0; e < kPer / 4; ++e) {
-      const float4 v = src[e];
-      acc[4 * e] += wt * v.x;
-      acc[4 * e + 1] += wt * v.y;
-      acc[4 * e + 2] += wt * v.z;
-      acc[4 * e + 3] += wt * v.w;
+  float wsum = 0.f, mrun = -INFINITY;
+  // contributions in batches of 16: lane `part` fetches (m, l) of one of them,
+  // then the 16 lanes accumulate every contribution's slice of o
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    const int k = k0 + part;
+    float m = -INFINITY, l = 0.f;
+    int w = 0;
+    if (k < n) {
+      const int32_t* cr = a.contribs + (int64_t)(tile[3] + a.clist[cs + k]) * kContribWords;
+      w = (rbase + cr[2] + t - cr[0]) * group + hh;
+      m = a.ws_ml[(int64_t)w * 2];
+      l = a.ws_ml[(int64_t)w * 2 + 1];
     }
-    wsum += wt;
+    float bm = l > 0.f ? m : -INFINITY;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 16));
+    const float mnew = fmaxf(mrun, bm);
+    if (mrun != -INFINITY && mnew != mrun) {
+      const float sc = exp2_fast(mrun - mnew);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[e] *= sc;
+      wsum *= sc;
+    }
+    mrun = mnew;
+    const float wt = l > 0.f ? l * exp2_fast(m - mnew) : 0.f;
+    const int cnt = min(16, n - k0);
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = __shfl(wt, j, 16);
+      const int wi = __shfl(w, j, 16);
+      if (wj == 0.f) continue;
+      const float4* src = reinterpret_cast<const float4*>(a.ws_o + (int64_t)wi * D + part * kPer);
+#pragma unroll
+      for (int e = 0; e < kPer / 4; ++e) {
+        const float4 v = src[e];
+        acc[4 * e] += wj * v.x;
+        acc[4 * e + 1] += wj * v.y;
+        acc[4 * e + 2] += wj * v.z;
+        acc[4 * e + 3] += wj * v.w;
+      }
+      wsum += wj;
+    }
   }
+  if (!live) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int32_t q_index = a.toks[(int64_t)(tile[0] + t) * kTokWords];
   T* dst = reinterpret_cast<T*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + hh) * D + part * kPer;
@@ -280,9 +300,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hi = lane >> 5;
   const int row = wave * 32 + li;  // this lane's query row in the tile
-  const bool row_ok = row < n_rows;
   const int tloc = row / group;    // tile-local token
-  const bool wave_live = wave * 32 < n_rows;
+  // tokens this item attends for: all of a direct tile, the contribution's
+  // range of a split tile
+  int act_lo = 0, act_hi = n_tok;
+  if (tile[4] >= 0) {
+    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+    act_lo = cr0[0];
+    act_hi = cr0[1];
+  }
+  const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
+  const bool wave_live = __ballot(row_ok) != 0;
 
   // ---- Q (B operand): Q[row][16 ks + 8 h .. +8) ----
   bf16x8 qreg[KSTEPS];
@@ -648,6 +676,9 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   if (p->ws_bytes > 0 && (!ws || ws_bytes < p->ws_bytes))
     return fail(RDX_EINVAL, "attention: workspace of %lld bytes needed", (long long)p->ws_bytes);
   const int64_t n_merge = (int64_t)(p->mblocks.size() / 2) * desc->num_kv_heads;
+  if (p->ws_tokens * desc->num_q_heads >= ((int64_t)1 << 31))
+    return fail(RDX_EUNSUPPORTED, "attention: split workspace too large (%lld partial rows)",
+                (long long)(p->ws_tokens * desc->num_q_heads));
   if (n_items > INT32_MAX || n_merge > INT32_MAX) return fail(RDX_EINVAL, "attention: too many work items");
   const int32_t* base = reinterpret_cast<const int32_t*>(dev_plan);
   AttnArgs a;
