@@ -117,6 +117,7 @@ int rdx_plan_create(const rdx_attn_desc* desc, int32_t kind, int32_t target_item
   p->desc = *desc;
   p->kind = kind;
   p->target_items = target_items;
+  if (kind == RDX_PLAN_EXTEND && desc->dtype == RDX_BF16 && desc->head_dim == 128) p->tile_rows = 2 * rdx::kTileRows;
   *out = reinterpret_cast<rdx_plan*>(p);
   return rdx::ok();
 }
@@ -159,7 +160,7 @@ int rdx_plan_get_view(const rdx_plan* plan, rdx_plan_view* out) {
   out->num_tokens = (int64_t)p->toks.size() / rdx::kTokWords;
   out->contribs = p->contribs.data();
   out->num_contribs = (int64_t)p->contribs.size() / rdx::kContribWords;
-  out->tile_rows = rdx::kTileRows;
+  out->tile_rows = p->tile_rows;
   out->group = p->group();
   return rdx::ok();
 }

@@ -264,6 +264,154 @@ struct KVTile {
   __bf16 vt[D * VS];
 };
 
+// max(x, x of lane ^ 32) via the gfx950 half-wave swap (a VALU op, no LDS)
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Scheduling hint for a run of N (LDS operand read, MFMA) pairs: issue
+// four reads first, then alternate one MFMA / one read, then the last four
+// MFMAs, so each MFMA finds its operand already loaded.
+template <int N>
+__device__ __forceinline__ void sched_lds_mfma() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < N - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, 4, 0);
+}
+
+// One 64-key block for one wave's 32 query rows: S^T = K Q^T on MFMA, mask
+// (keys with block-local index >= rel are invisible to this lane's row),
+// online softmax in base 2 with lazy rescale, O^T += V^T P^T on MFMA.
+template <int D>
+__device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qreg)[D / 16], f32x16 (&acc)[D / 32],
+                                           float& m_run, float& l_run, int rel, float c2, int li, int hi) {
+  constexpr int KS = KVTile<D>::KS, VS = KVTile<D>::VS;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  // S^T = K Q^T for 64 keys x this wave's 32 queries.  The two 32-key
+  // halves are interleaved (independent accumulators) and the scheduler is
+  // told to keep LDS operand reads several MFMAs ahead.
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t.k[(32 * kb2 + li) * KS + 16 * ks + 8 * hi]);
+      s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb2], 0, 0, 0);
+    }
+  sched_lds_mfma<2 * KSTEPS>();
+  // mask (only where some lane of the wave needs it) + online softmax, base 2
+    if (__ballot(rel < 64)) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 32 * kb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[kb2][r] = kl < rel ? s[kb2][r] : -INFINITY;
+      }
+  }
+  // row max: four independent chains, then the other half-wave via permlane32 swap
+  float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mxp[r & 3] = fmaxf(mxp[r & 3], s[kb2][r]);
+  float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
+  mx = half_swap_max(mx);
+  // Lazy rescale: the running max moves only when a score exceeds it by
+  // more than 2^8, so probabilities stay <= 256 (exact: the same stale
+  // max scales numerator and denominator) and most blocks skip the
+  // O rescale.
+  const float t_max = mx * c2;
+  const float m_new = t_max > m_run + 8.f ? t_max : m_run;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2_fast(m_run - m_use);
+  float lsp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[kb2][r], c2, -m_use));
+      s[kb2][r] = p;
+      lsp[r & 3] += p;
+    }
+  const float lsum = (lsp[0] + lsp[1]) + (lsp[2] + lsp[3]);
+  l_run = l_run * alpha + lsum;
+  m_run = m_new;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+  }
+  // P (B operand): 16-key step ks uses registers 8t..8t+7 of block ks/2
+  bf16x8 pk[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
+  // O^T += V^T P^T (d blocks interleaved: independent accumulators)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&t.vt[(32 * db + li) * VS + 16 * ks + 8 * hi]);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], acc[db], 0, 0, 0);
+    }
+  sched_lds_mfma<4 * DB>();
+
+}
+
+// Final result of one lane's row: the normalised output (direct tiles) or
+// the partial state (split tiles, contribution item[4]).
+template <int D>
+__device__ __forceinline__ void write_result(const AttnArgs& a, const int32_t* tile, const int32_t* item, int kvh,
+                                             const f32x16 (&acc)[D / 32], float m_run, float l_run, bool row_ok,
+                                             int tloc, int row, int hi) {
+  constexpr int DB = D / 32;
+  const int group = a.group, tok_begin = tile[0];
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (tile[4] < 0) {
+    if (row_ok) {
+      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
+      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hi) = v;
+        }
+    }
+    return;
+  }
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+    float* dst = a.ws_o + w * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g4 + 4 * hi) =
+            make_float4(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv, acc[db][4 * g4 + 2] * inv,
+                        acc[db][4 * g4 + 3] * inv);
+    if (hi == 0) {
+      a.ws_ml[w * 2] = m_run;
+      a.ws_ml[w * 2 + 1] = l_tot;
+    }
+  }
+
+}
+
 template <int D, bool OFF32>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ KVTile<D> buf[2];
@@ -406,73 +554,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       }
       const KVTile<D>& t = buf[b & 1];
       if (wave_job) {
-        // S^T = K Q^T for 64 keys x this wave's 32 queries
-        f32x16 s[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          s[kb2] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < KSTEPS; ++ks) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t.k[(32 * kb2 + li) * KS + 16 * ks + 8 * hi]);
-            s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb2], 0, 0, 0);
-          }
-        }
-        // mask (only where some lane of the wave needs it) + online softmax, base 2
-        const int rel = lim - it_comp.kb;  // keys with local index < rel are visible
-        if (__ballot(rel < 64)) {
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kl = 32 * kb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              s[kb2][r] = kl < rel ? s[kb2][r] : -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Lazy rescale: the running max moves only when a score exceeds it by
-        // more than 2^8, so probabilities stay <= 256 (exact: the same stale
-        // max scales numerator and denominator) and most blocks skip the
-        // O rescale.
-        const float t_max = mx * c2;
-        const float m_new = t_max > m_run + 8.f ? t_max : m_run;
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = exp2_fast(fmaf(s[kb2][r], c2, -m_use));
-            s[kb2][r] = p;
-            lsum += p;
-          }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        }
-        // P (B operand): 16-key step ks uses registers 8t..8t+7 of block ks/2
-        bf16x8 pk[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
-        // O^T += V^T P^T
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(&t.vt[(32 * db + li) * VS + 16 * ks + 8 * hi]);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], acc[db], 0, 0, 0);
-          }
+        wave_block<D>(t, qreg, acc, m_run, l_run, lim - it_comp.kb, c2, li, hi);
       }
       // ---- block b+1 into the other buffer ----
       if (b + 1 < nblk) store_kv(buf[(b + 1) & 1]);
@@ -482,41 +564,146 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (tile[4] < 0) {
-    if (row_ok) {
-      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
-      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hi) = v;
-        }
-    }
-    return;
+  write_result<D>(a, tile, item, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
+}
+
+// ---------------------------------------------------------------------------
+// Wide bf16 extend kernel (head_dim 128): 8 waves, 256-row tiles.  Each K/V
+// block feeds twice the rows of the 4-wave kernel (half the loads, LDS stores
+// and barriers per flop), and each thread stages only one unit (waves 0-3 K,
+// waves 4-7 V), which leaves registers for two blocks of prefetch: at block
+// b the K/V rows of block b+2 are being loaded, block b+1 waits in registers,
+// and the page-table slots of block b+3 are read.
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 512;
+
+template <bool OFF32>
+__global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArgs a) {
+  constexpr int D = 128, KSTEPS = D / 16, DB = D / 32, CH = D / 8;
+  __shared__ KVTile<D> buf[2];
+  __shared__ int slot_ring[2][64];
+
+  const int tid = threadIdx.x;
+  const bool doK = tid < 256;
+  const int u = tid & 255;
+  const int qd = doK ? u / CH : u % 16;  // K units: chunk fastest; V units: key quad fastest
+  const int cc = doK ? u % CH : u / 16;
+
+  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
+  const int kvh = item[1];
+  const int jb = item[2], je = item[3];
+  const int tok_begin = tile[0], n_tok = tile[1];
+  const int group = a.group;
+  const int n_rows = n_tok * group;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int row = wave * 32 + li;
+  const int tloc = row / group;
+  int act_lo = 0, act_hi = n_tok;
+  if (tile[4] >= 0) {
+    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+    act_lo = cr0[0];
+    act_hi = cr0[1];
   }
-  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
-  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
-    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
-    float* dst = a.ws_o + w * D;
+  const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
+  const bool wave_live = __ballot(row_ok) != 0;
+
+  bf16x8 qreg[KSTEPS];
+  int qpos = 0;
+  if (row_ok) {
+    const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
+    qpos = tk[1];
+    const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
+                        ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int s = 0; s < KSTEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+  } else {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g4 + 4 * hi) =
-            make_float4(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv, acc[db][4 * g4 + 2] * inv,
-                        acc[db][4 * g4 + 3] * inv);
-    if (hi == 0) {
-      a.ws_ml[w * 2] = m_run;
-      a.ws_ml[w * 2 + 1] = l_tot;
+    for (int s = 0; s < KSTEPS; ++s) qreg[s] = bf16x8{};
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  PoolReader<OFF32> pool;
+  pool.init(doK ? a.kp : a.vp, a.pool_bytes, (uint32_t)(a.hkv * D * 2));
+  const uint32_t off = (uint32_t)(kvh * D + 8 * cc) * 2;
+  const int vcol = vt_col(qd);
+
+  int nblk = 0;
+  for (int j = jb; j < je; ++j) {
+    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+    nblk += (job[2] - job[1] + 63) >> 6;
+  }
+
+  auto issue = [&](Rows4& r, const int* slots) {
+    const int4 sl = *reinterpret_cast<const int4*>(slots + 4 * qd);
+    r = pool.rows(sl, off);
+  };
+  auto stage = [&](KVTile<D>& t, const Rows4& r) {
+    if (doK)
+      store_k_rows<D>(t.k, r, qd, cc);
+    else
+      store_vt_rows<D>(t.vt, r, cc, vcol);
+  };
+
+  if (nblk > 0) {
+    BlockIter it_slot, it_comp;
+    iter_job(a, it_slot, jb);
+    it_comp = it_slot;
+    Rows4 rA, rB;
+    // ---- prologue: block 0 in LDS, block 1 in registers, slots of block 2 in the ring ----
+    if (tid < 64) slot_ring[0][tid] = block_slot(it_slot, tid);
+    iter_next(a, it_slot, je);
+    if (nblk > 1) {
+      if (tid < 64) slot_ring[1][tid] = block_slot(it_slot, tid);
+      iter_next(a, it_slot, je);
+    }
+    __syncthreads();
+    issue(rA, slot_ring[0]);
+    if (nblk > 1) issue(rB, slot_ring[1]);
+    __syncthreads();
+    if (nblk > 2) {
+      if (tid < 64) slot_ring[0][tid] = block_slot(it_slot, tid);
+      iter_next(a, it_slot, je);
+    }
+    stage(buf[0], rA);
+    __syncthreads();
+
+    int cur_job = -1, lim = 0;
+    bool wave_job = false;
+    // one key block: rcur holds nothing live (it is reloaded with block b+2),
+    // rnext holds block b+1 (staged into LDS after the compute)
+    auto step = [&](int b, Rows4& rcur, Rows4& rnext) {
+      if (b + 2 < nblk) issue(rcur, slot_ring[b & 1]);
+      int slot_after = 0;
+      const bool more = b + 3 < nblk;
+      if (more) {
+        if (tid < 64) slot_after = block_slot(it_slot, tid);
+        iter_next(a, it_slot, je);
+      }
+      if (it_comp.j != cur_job) {
+        cur_job = it_comp.j;
+        const int32_t* job = a.jobs + (int64_t)cur_job * kJobWords;
+        const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+        lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+        wave_job = wave_live && __ballot(lim > job[1]) != 0;
+      }
+      if (wave_job) wave_block<D>(buf[b & 1], qreg, acc, m_run, l_run, lim - it_comp.kb, c2, li, hi);
+      if (b + 1 < nblk) stage(buf[(b + 1) & 1], rnext);
+      if (more && tid < 64) slot_ring[(b + 1) & 1][tid] = slot_after;
+      iter_next(a, it_comp, je);
+      __syncthreads();
+    };
+    for (int b = 0; b < nblk; b += 2) {
+      step(b, rA, rB);
+      if (b + 1 < nblk) step(b + 1, rB, rA);
     }
   }
+  write_result<D>(a, tile, item, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,7 +807,7 @@ struct Timing {
 // event and the last one the stop event (events bound to the dispatches).
 template <typename KA, typename KM>
 hipError_t launch(KA attn, KM merge, int64_t n_items, int64_t n_merge, hipStream_t st, int32_t kind,
-                  const AttnArgs& a) {
+                  const AttnArgs& a, int threads = kThreads) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (g_timing.on && g_timing.used < g_timing.cap) {
     const int32_t i = g_timing.used;
@@ -639,11 +826,11 @@ hipError_t launch(KA attn, KM merge, int64_t n_items, int64_t n_merge, hipStream
     e0 = g_timing.start[i];
     e1 = g_timing.stop[i];
   }
-  const dim3 block(kThreads);
+  const dim3 block(kThreads), ablock(threads);
   if (e0)
-    hipExtLaunchKernelGGL(attn, dim3((unsigned)n_items), block, 0, st, e0, n_merge ? nullptr : e1, 0, a);
+    hipExtLaunchKernelGGL(attn, dim3((unsigned)n_items), ablock, 0, st, e0, n_merge ? nullptr : e1, 0, a);
   else
-    hipLaunchKernelGGL(attn, dim3((unsigned)n_items), block, 0, st, a);
+    hipLaunchKernelGGL(attn, dim3((unsigned)n_items), ablock, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_merge == 0) return e;
   if (e1)
@@ -711,7 +898,12 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   // pools under 2 GiB are addressed with 32-bit buffer offsets (the buffer
   // resource's record count is a signed 32-bit value here)
   const bool off32 = a.pool_bytes < ((int64_t)1 << 31);
-  if (desc->dtype == RDX_BF16) {
+  if (desc->dtype == RDX_BF16 && p->tile_rows == 256) {
+    e = off32 ? launch(attn_bf16_wide_kernel<true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a,
+                       kWideThreads)
+              : launch(attn_bf16_wide_kernel<false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a,
+                       kWideThreads);
+  } else if (desc->dtype == RDX_BF16) {
     if (desc->head_dim == 128)
       e = off32 ? launch(attn_bf16_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a)
                 : launch(attn_bf16_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a);

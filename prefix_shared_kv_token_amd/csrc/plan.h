@@ -52,8 +52,11 @@ struct Plan {
   void* event = nullptr;
   bool upload_pending = false;
 
+  // query rows per tile: 256 for the wide bf16 head_dim-128 extend kernel,
+  // kTileRows otherwise
+  int tile_rows = kTileRows;
   int group() const { return desc.num_q_heads / desc.num_kv_heads; }
-  int tile_tokens() const { return kTileRows / group(); }
+  int tile_tokens() const { return tile_rows / group(); }
   int build(const RadixTree& tree, const rdx_batch& b, int64_t ld);
   void layout();
 };
