@@ -17,9 +17,11 @@ in the timed region on the launch stream.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -29,6 +31,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
+KERNEL_SOURCES = ("prefix_shared_kv_token_amd/csrc/attn_kernels.h", "prefix_shared_kv_token_amd/csrc/plan.h",
+                  "prefix_shared_kv_token_amd/csrc/plan.cpp")
 
 
 def extend_flops(cfg, phase_reqs):
@@ -53,6 +57,31 @@ def decode_bytes(wl, t):
     kv = rows * 2 * cfg.n_kv_heads * cfg.head_dim * b
     qo = 2 * len(leaves) * cfg.n_q_heads * cfg.head_dim * b
     return kv + qo + 4 * rows
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources and the planner that shapes their
+    launches; a counter summary taken from other sources does not apply."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/<kind>_attention_<workload>_traffic.md), or None when there is
+    none or it was taken from different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_attention_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_src or not m_val or m_src.group(1) != kernel_source_digest():
+        return None
+    return {"bytes_per_launch": int(m_val.group(1)), "source": os.path.relpath(path, ROOT)}
 
 
 def cpu_baseline(wl, seconds: float):
@@ -146,12 +175,17 @@ def main():
         run.run(keep_outputs=False)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms, kinds = rdx.timing_read(n_launch)
-    assert len(ms) == n_launch, (len(ms), n_launch)
+    attn_ms, merge_ms, kinds = rdx.timing_read(n_launch)
+    assert len(attn_ms) == n_launch, (len(attn_ms), n_launch)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # ---- per-launch kernel durations (ms), reshaped [steps, launches/step] ----
-    per_step = ms.reshape(args.steps, -1)
+    # an attention launch = its attention kernel + the merge kernel behind it
+    # (when the plan split tiles); both durations come from events bound to
+    # the dispatches, so their sum excludes the gap between the two
+    a_step = attn_ms.reshape(args.steps, -1)
+    m_step = merge_ms.reshape(args.steps, -1)
+    per_step = a_step + m_step
     n_ph = len(wl.phases)
     # launch order per step: extend of phase 0 .. extend of last phase, decode steps after the last extend
     ext_ms = per_step[:, :n_ph]
@@ -166,17 +200,31 @@ def main():
     R = len(wl.leaf_requests)
     tokens_per_step = sum(run.extend_tokens) + run.decode_tokens
 
+    def kernel_us(cols):
+        return {"attention_kernel_us": float(a_step[:, cols].mean() * 1e3),
+                "merge_kernel_us": float(m_step[:, cols].mean() * 1e3)}
+
     ext_tflops = ext_flops / ext_member_s / 1e12
     peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    n_mem = len(member_phases)
     extend_roof = {"bound": "mfma", "achieved": ext_tflops, "peak": peak_tf, "unit": "TFLOP/s",
                    "frac": ext_tflops / peak_tf, "traffic": None,
-                   "avg_launch_us": ext_member_s * 1e6 / len(member_phases),
-                   "work_per_step": f"{ext_flops / 1e9:.2f} GFLOP over {member_tokens} member query tokens"}
+                   "avg_launch_us": ext_member_s * 1e6 / n_mem, **kernel_us(member_phases),
+                   "work_per_launch": f"{ext_flops / n_mem / 1e9:.2f} GFLOP "
+                                      f"({member_tokens / n_mem:.0f} member query tokens)"}
+    dec_cols = list(range(n_ph, per_step.shape[1]))
     dec_gbs = dec_bytes / dec_total_s / 1e9 if dec_total_s else 0.0
     decode_roof = {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": dec_gbs / PEAK_HBM_GBS, "traffic": None,
                    "avg_launch_us": dec_total_s * 1e6 / max(1, cfg.decode_steps),
-                   "work_per_step": f"{dec_bytes / 1e9:.3f} GB over {cfg.decode_steps} launches"}
+                   **(kernel_us(dec_cols) if dec_cols else {}),
+                   "work_per_launch": f"{dec_bytes / max(1, cfg.decode_steps) / 1e6:.1f} MB (mean over "
+                                      f"{cfg.decode_steps} decode steps)"}
+    for kname, roof in (("extend", extend_roof), ("decode", decode_roof)):
+        t = measured_traffic(kname, cfg.name)
+        if t is not None:
+            roof["traffic"] = t["bytes_per_launch"]
+            roof["traffic_source"] = t["source"]
     dominant = decode_roof if dec_total_s >= ext_ms.sum(axis=1).mean() / 1e3 else extend_roof
     dominant = dict(dominant, kernel="decode attention" if dominant is decode_roof else "extend attention")
 

@@ -244,14 +244,18 @@ int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const 
 
 /* ------------------------------------------------------- launch timing */
 /* For benchmarks.  rdx_timing_begin(cap) starts recording: the next (up to
- * cap) attention launches are issued with HIP events bound to the kernel
- * dispatch itself (hipExtLaunchKernel), so time the GPU spends waiting for
- * the host between launches is not counted.  rdx_timing_read waits for the
- * recorded launches, writes their durations in milliseconds and kinds
- * (RDX_PLAN_EXTEND / RDX_PLAN_DECODE) in launch order (capacity cap), sets
- * *out_n, and stops recording.  Errors: EINVAL, EDEVICE. */
+ * cap) attention launches are issued with HIP events bound to each kernel
+ * dispatch itself (hipExtLaunchKernel) -- one pair on the attention kernel,
+ * one on the merge kernel when the plan has split tiles -- so time the GPU
+ * spends between dispatches is not counted.  rdx_timing_read waits for the
+ * recorded launches and writes, in launch order (capacity cap), each
+ * attention kernel's duration in milliseconds to out_attn_ms, the merge
+ * kernel's (0 when none ran) to out_merge_ms (may be NULL) and the kind
+ * (RDX_PLAN_EXTEND / RDX_PLAN_DECODE) to out_kind; it sets *out_n and stops
+ * recording.  Errors: EINVAL, EDEVICE. */
 int rdx_timing_begin(int32_t cap);
-int rdx_timing_read(float* out_ms, int32_t* out_kind, int32_t cap, int32_t* out_n);
+int rdx_timing_read(float* out_attn_ms, float* out_merge_ms, int32_t* out_kind, int32_t cap,
+                    int32_t* out_n);
 
 #ifdef __cplusplus
 }

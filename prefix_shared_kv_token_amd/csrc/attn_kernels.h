@@ -1,0 +1,793 @@
+// Device code of librdx for gfx950 (CDNA4): the prefix-shared attention
+// kernels, the merge of split tiles, KV scatter and page-table writes.
+// Included by exactly one translation unit (device.hip), which holds the
+// host-side launch code.
+//
+// Attention follows the BatchLLM explainer, Horizontal Fusion section: the
+// common-prefix part and each request's own part of prefix-shared attention
+// are work of one kernel -- a row tile streams the shared-prefix keys and its
+// requests' own keys, carrying one online-softmax state across both -- and
+// when a tile's key ranges are split over several workgroups, their partial
+// softmax states (o, running max m, running sum l) are combined with the
+// log-sum-exp rule
+//   M = max_c m_c,  w_c = l_c 2^(m_c - M),  o = sum_c w_c o_c / sum_c w_c
+// (scores kept in the base-2 domain: t = s * scale * log2 e) by a merge pass
+// queued right behind the attention kernel.
+#pragma once
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "plan.h"
+
+namespace rdx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;  // 4 waves of 64; wave w owns tile rows [32w, 32w+32)
+
+struct AttnArgs {
+  const int32_t* items;
+  const int32_t* tiles;
+  const int32_t* jobs;
+  const int32_t* toks;
+  const int32_t* contribs;
+  const int32_t* cptr;
+  const int32_t* clist;
+  const int32_t* mblocks;
+  const int32_t* page_table;
+  int64_t ld;
+  const void* q;
+  const void* kp;
+  const void* vp;
+  void* o;
+  float* ws_o;
+  float* ws_ml;
+  int64_t ws_tokens;
+  int64_t pool_bytes;  // bytes of each KV pool
+  int hq, hkv, group;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(__bf16* p, float v) { *p = (__bf16)v; }
+
+// ---------------------------------------------------------------------------
+// Merge of split tiles.  A contribution's partial for (tile token t, grouped
+// head hh) lives at
+//   ws_o [((kvh * ws_tokens + base + t - lo) * group + hh) * D + d]
+//   ws_ml[((kvh * ws_tokens + base + t - lo) * group + hh) * 2 + {0: m, 1: l}]
+// with o already normalised by its own l.  Each workgroup merges 16 query
+// rows of one split tile for one KV head (16 lanes per row, D/16 values per
+// lane), visiting only the contributions that cover the row's token.  It
+// runs after the attention kernel in stream order.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
+  constexpr int kPer = D / 16;  // values per lane
+  const int32_t* mb = a.mblocks + (int64_t)(blockIdx.x / a.hkv) * 2;
+  const int kvh = blockIdx.x % a.hkv;
+  const int32_t* tile = a.tiles + (int64_t)mb[0] * kTileWords;
+  const int group = a.group;
+  const int row = mb[1] + threadIdx.x / 16;
+  const int part = threadIdx.x % 16;
+  const bool live = row < tile[1] * group;  // 16-lane groups stay whole for the shuffles
+  const int t = live ? row / group : 0, hh = live ? row % group : 0;
+  const int32_t* cp = a.cptr + tile[5] + t;
+  const int cs = live ? cp[0] : 0, n = live ? cp[1] - cp[0] : 0;
+  const int rbase = kvh * (int)a.ws_tokens;
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  float wsum = 0.f, mrun = -INFINITY;
+  // contributions in batches of 16: lane `part` fetches (m, l) of one of them,
+  // then the 16 lanes accumulate every contribution's slice of o
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    const int k = k0 + part;
+    float m = -INFINITY, l = 0.f;
+    int w = 0;
+    if (k < n) {
+      const int32_t* cr = a.contribs + (int64_t)(tile[3] + a.clist[cs + k]) * kContribWords;
+      w = (rbase + cr[2] + t - cr[0]) * group + hh;
+      m = a.ws_ml[(int64_t)w * 2];
+      l = a.ws_ml[(int64_t)w * 2 + 1];
+    }
+    float bm = l > 0.f ? m : -INFINITY;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 16));
+    const float mnew = fmaxf(mrun, bm);
+    if (mrun != -INFINITY && mnew != mrun) {
+      const float sc = exp2_fast(mrun - mnew);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[e] *= sc;
+      wsum *= sc;
+    }
+    mrun = mnew;
+    const float wt = l > 0.f ? l * exp2_fast(m - mnew) : 0.f;
+    const int cnt = min(16, n - k0);
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = __shfl(wt, j, 16);
+      const int wi = __shfl(w, j, 16);
+      if (wj == 0.f) continue;
+      const float4* src = reinterpret_cast<const float4*>(a.ws_o + (int64_t)wi * D + part * kPer);
+#pragma unroll
+      for (int e = 0; e < kPer / 4; ++e) {
+        const float4 v = src[e];
+        acc[4 * e] += wj * v.x;
+        acc[4 * e + 1] += wj * v.y;
+        acc[4 * e + 2] += wj * v.z;
+        acc[4 * e + 3] += wj * v.w;
+      }
+      wsum += wj;
+    }
+  }
+  if (!live) return;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int32_t q_index = a.toks[(int64_t)(tile[0] + t) * kTokWords];
+  T* dst = reinterpret_cast<T*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + hh) * D + part * kPer;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_out(dst + e, acc[e] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Iteration over the 64-key blocks of a work item's jobs.
+// ---------------------------------------------------------------------------
+struct BlockIter {
+  int j, kb, k1;
+  const int32_t* prow;
+};
+
+__device__ __forceinline__ void iter_job(const AttnArgs& a, BlockIter& it, int j) {
+  const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+  it.j = j;
+  it.prow = a.page_table + (int64_t)job[0] * a.ld;
+  it.kb = job[1];
+  it.k1 = job[2];
+}
+
+__device__ __forceinline__ void iter_next(const AttnArgs& a, BlockIter& it, int je) {
+  it.kb += 64;
+  if (it.kb >= it.k1 && it.j + 1 < je) iter_job(a, it, it.j + 1);
+}
+
+// Slot of key `i` of the block.  Positions past the job's end read the
+// job's last position instead (a valid slot); those keys are masked out of
+// the softmax, so their K/V rows only cost bandwidth.
+__device__ __forceinline__ int block_slot(const BlockIter& it, int i) {
+  return it.prow[min(it.kb + i, it.k1 - 1)];
+}
+
+// ---------------------------------------------------------------------------
+// K/V tile staging helpers (4 key rows x one 16-byte chunk per unit)
+// ---------------------------------------------------------------------------
+struct Rows4 {
+  uint4 a, b, c, d;
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Reads 16-byte chunks of pool rows.  OFF32: the pool is under 4 GiB and is
+// addressed through a raw buffer resource with 32-bit byte offsets
+// (slot * row_bytes + chunk offset, a 24-bit multiply since such a pool has
+// fewer than 2^24 rows); otherwise 64-bit pointer arithmetic.
+template <bool OFF32>
+struct PoolReader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  const char* base;
+  uint32_t row_bytes;
+  __device__ void init(const void* pool, int64_t pool_bytes, uint32_t rb) {
+    base = reinterpret_cast<const char*>(pool);
+    row_bytes = rb;
+    if constexpr (OFF32) rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(pool), (short)0, (int)pool_bytes, 0x00020000);
+  }
+  __device__ __forceinline__ uint4 chunk(int slot, uint32_t off) const {
+    if constexpr (OFF32) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(__umul24((uint32_t)slot, row_bytes) + off), 0, 0);
+      return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+      return *reinterpret_cast<const uint4*>(base + (int64_t)slot * row_bytes + off);
+    }
+  }
+  __device__ __forceinline__ Rows4 rows(const int4& s, uint32_t off) const {
+    Rows4 r;
+    r.a = chunk(s.x, off);
+    r.b = chunk(s.y, off);
+    r.c = chunk(s.z, off);
+    r.d = chunk(s.w, off);
+    return r;
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void store_k_rows(__bf16* k, const Rows4& r, int qd, int cc) {
+  constexpr int KS = D + 8;
+  __bf16* p = k + (4 * qd) * KS + 8 * cc;
+  *reinterpret_cast<uint4*>(p) = r.a;
+  *reinterpret_cast<uint4*>(p + KS) = r.b;
+  *reinterpret_cast<uint4*>(p + 2 * KS) = r.c;
+  *reinterpret_cast<uint4*>(p + 3 * KS) = r.d;
+}
+
+// V^T column of key quad qd: quads are stored in the MFMA contraction order
+// (within each 16 keys: quads 0, 2, 1, 3)
+__device__ __forceinline__ int vt_col(int qd) {
+  const int qk = qd & 3;
+  return 16 * (qd >> 2) + 4 * (qk == 1 ? 2 : (qk == 2 ? 1 : qk));
+}
+
+// 4 keys x 8 d of V -> 8 rows (d = 8 cc ..) x 4 keys of V^T
+__device__ __forceinline__ void vt_pair(__bf16* vt, int vs, int d, int col, uint32_t w0, uint32_t w1, uint32_t w2,
+                                        uint32_t w3) {
+  // low halves of (w0, w1) and (w2, w3) -> row d; high halves -> row d + 1
+  const uint2 lo2 = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u));
+  const uint2 hi2 = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u));
+  *reinterpret_cast<uint2*>(vt + d * vs + col) = lo2;
+  *reinterpret_cast<uint2*>(vt + (d + 1) * vs + col) = hi2;
+}
+
+template <int D>
+__device__ __forceinline__ void store_vt_rows(__bf16* vt, const Rows4& r, int cc, int col) {
+  constexpr int VS = 64 + 8;
+  const int d = 8 * cc;
+  vt_pair(vt, VS, d, col, r.a.x, r.b.x, r.c.x, r.d.x);
+  vt_pair(vt, VS, d + 2, col, r.a.y, r.b.y, r.c.y, r.d.y);
+  vt_pair(vt, VS, d + 4, col, r.a.z, r.b.z, r.c.z, r.d.z);
+  vt_pair(vt, VS, d + 6, col, r.a.w, r.b.w, r.c.w, r.d.w);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel.  One workgroup per work item (tile, KV head, key ranges).
+// Wave w holds query rows 32w..32w+31 of the tile; lane (i = lane % 32,
+// h = lane / 32).  Scores are computed transposed, S^T = K Q^T, with the
+// 32x32x16 bf16 MFMA so that each lane owns one query column: the row max is
+// a reduction over the lane's registers plus one exchange with lane ^ 32, and
+// the probabilities feed the P.V MFMA (O^T = V^T P^T) straight from
+// registers.  The contraction order inside a 16-key step is permuted
+// identically on both operands: lane half h holds keys {4h..4h+3, 8+4h..
+// 8+4h+3}; V^T is stored in LDS with its key quads in that order.
+//
+// Pipeline: page-table slots are fetched two key blocks ahead and K/V rows
+// one block ahead into registers while the MFMAs of the current block run;
+// K and V^T live in a double-buffered LDS tile, one barrier per block.
+// ---------------------------------------------------------------------------
+template <int D>
+struct KVTile {
+  static constexpr int KS = D + 8;   // K tile row stride (elements), padded
+  static constexpr int VS = 64 + 8;  // V^T tile row stride
+  __bf16 k[64 * KS];
+  __bf16 vt[D * VS];
+};
+
+// max(x, x of lane ^ 32) via the gfx950 half-wave swap (a VALU op, no LDS)
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Scheduling hint for a run of N (LDS operand read, MFMA) pairs: issue
+// four reads first, then alternate one MFMA / one read, then the last four
+// MFMAs, so each MFMA finds its operand already loaded.
+template <int N>
+__device__ __forceinline__ void sched_lds_mfma() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < N - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, 4, 0);
+}
+
+// One 64-key block for one wave's 32 query rows: S^T = K Q^T on MFMA, mask
+// (keys with block-local index >= rel are invisible to this lane's row),
+// online softmax in base 2 with lazy rescale, O^T += V^T P^T on MFMA.
+template <int D>
+__device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qreg)[D / 16], f32x16 (&acc)[D / 32],
+                                           float& m_run, float& l_run, int rel, float c2, int li, int hi) {
+  constexpr int KS = KVTile<D>::KS, VS = KVTile<D>::VS;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  // S^T = K Q^T for 64 keys x this wave's 32 queries.  The two 32-key
+  // halves are interleaved (independent accumulators) and the scheduler is
+  // told to keep LDS operand reads several MFMAs ahead.
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t.k[(32 * kb2 + li) * KS + 16 * ks + 8 * hi]);
+      s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb2], 0, 0, 0);
+    }
+  sched_lds_mfma<2 * KSTEPS>();
+  // mask (only where some lane of the wave needs it) + online softmax, base 2
+    if (__ballot(rel < 64)) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 32 * kb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[kb2][r] = kl < rel ? s[kb2][r] : -INFINITY;
+      }
+  }
+  // row max: four independent chains, then the other half-wave via permlane32 swap
+  float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mxp[r & 3] = fmaxf(mxp[r & 3], s[kb2][r]);
+  float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
+  mx = half_swap_max(mx);
+  // Lazy rescale: the running max moves only when a score exceeds it by
+  // more than 2^8, so probabilities stay <= 256 (exact: the same stale
+  // max scales numerator and denominator) and most blocks skip the
+  // O rescale.
+  const float t_max = mx * c2;
+  const float m_new = t_max > m_run + 8.f ? t_max : m_run;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2_fast(m_run - m_use);
+  float lsp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[kb2][r], c2, -m_use));
+      s[kb2][r] = p;
+      lsp[r & 3] += p;
+    }
+  const float lsum = (lsp[0] + lsp[1]) + (lsp[2] + lsp[3]);
+  l_run = l_run * alpha + lsum;
+  m_run = m_new;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+  }
+  // P (B operand): 16-key step ks uses registers 8t..8t+7 of block ks/2
+  bf16x8 pk[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
+  // O^T += V^T P^T (d blocks interleaved: independent accumulators)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&t.vt[(32 * db + li) * VS + 16 * ks + 8 * hi]);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], acc[db], 0, 0, 0);
+    }
+  sched_lds_mfma<4 * DB>();
+
+}
+
+// Final result of one lane's row: the normalised output (direct tiles) or
+// the partial state (split tiles, contribution item[4]).
+template <int D>
+__device__ __forceinline__ void write_result(const AttnArgs& a, const int32_t* tile, const int32_t* item, int kvh,
+                                             const f32x16 (&acc)[D / 32], float m_run, float l_run, bool row_ok,
+                                             int tloc, int row, int hi) {
+  constexpr int DB = D / 32;
+  const int group = a.group, tok_begin = tile[0];
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (tile[4] < 0) {
+    if (row_ok) {
+      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
+      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hi) = v;
+        }
+    }
+    return;
+  }
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+    float* dst = a.ws_o + w * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g4 + 4 * hi) =
+            make_float4(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv, acc[db][4 * g4 + 2] * inv,
+                        acc[db][4 * g4 + 3] * inv);
+    if (hi == 0) {
+      a.ws_ml[w * 2] = m_run;
+      a.ws_ml[w * 2 + 1] = l_tot;
+    }
+  }
+
+}
+
+template <int D, bool OFF32>
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+  __shared__ KVTile<D> buf[2];
+  __shared__ int4 slot_buf[2][16];  // page-table slots of the next two key blocks
+  constexpr int KS = KVTile<D>::KS, VS = KVTile<D>::VS;
+  constexpr int KSTEPS = D / 16;  // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;      // 32-wide d blocks of the output
+  constexpr int CH = D / 8;       // 16-byte chunks per K/V row
+  constexpr int UNITS = 16 * CH;  // (key quad, chunk) units per matrix
+  constexpr bool BOTH = 2 * UNITS > kThreads;  // each thread loads K and V of one unit
+
+  // Load units: a unit is (key quad qd, 16-byte chunk cc) of the 64 x D tile.
+  // K units vary cc fastest (16 lanes read one contiguous key row; row-major
+  // LDS stores).  V units vary qd fastest so that 16 consecutive lanes store
+  // 16 different 8-byte key quads of one V^T row (no LDS bank conflicts).
+  // head_dim 128: every thread loads one K and one V unit; 64: threads
+  // 0..127 load K, 128..255 load V (wave-uniform).
+  const int tid = threadIdx.x;
+  const bool doK = BOTH || tid < UNITS;
+  const bool doV = BOTH || tid >= UNITS;
+  const int uk = tid % UNITS;
+  const int uv = BOTH ? tid : tid - UNITS;
+  const int qd_k = uk / CH, cc_k = uk % CH;
+  const int qd_v = uv % 16, cc_v = uv / 16;
+  const int qd1 = doK ? qd_k : qd_v;  // the unit whose slots feed kr (head_dim 64: this thread's only unit)
+
+  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
+  const int kvh = item[1];
+  const int jb = item[2], je = item[3];
+  const int tok_begin = tile[0], n_tok = tile[1];
+  const int group = a.group;
+  const int n_rows = n_tok * group;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int row = wave * 32 + li;  // this lane's query row in the tile
+  const int tloc = row / group;    // tile-local token
+  // tokens this item attends for: all of a direct tile, the contribution's
+  // range of a split tile
+  int act_lo = 0, act_hi = n_tok;
+  if (tile[4] >= 0) {
+    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+    act_lo = cr0[0];
+    act_hi = cr0[1];
+  }
+  const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
+  const bool wave_live = __ballot(row_ok) != 0;
+
+  // ---- Q (B operand): Q[row][16 ks + 8 h .. +8) ----
+  bf16x8 qreg[KSTEPS];
+  int qpos = 0;
+  {
+    const __bf16* q = reinterpret_cast<const __bf16*>(a.q);
+    if (row_ok) {
+      const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
+      qpos = tk[1];
+      const __bf16* src = q + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qreg[s] = bf16x8{};
+    }
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  const uint32_t row_bytes = (uint32_t)(a.hkv * D * 2);
+  PoolReader<OFF32> kpool, vpool;
+  kpool.init(a.kp, a.pool_bytes, row_bytes);
+  vpool.init(a.vp, a.pool_bytes, row_bytes);
+  const uint32_t off1 = (uint32_t)(kvh * D + 8 * (doK ? cc_k : cc_v)) * 2;
+  const uint32_t off2 = (uint32_t)(kvh * D + 8 * cc_v) * 2;
+
+  int nblk = 0;
+  for (int j = jb; j < je; ++j) {
+    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+    nblk += (job[2] - job[1] + 63) >> 6;
+  }
+
+  // r1: rows of the thread's first unit (K; head_dim 64: K or V, whichever
+  // this thread loads); r2: rows of its V unit (head_dim 128 only).
+  Rows4 r1, r2;
+  const PoolReader<OFF32>& pool1 = doK ? kpool : vpool;
+  auto load_kv = [&](const int4 (&sb)[16]) {
+    r1 = pool1.rows(sb[qd1], off1);
+    if constexpr (BOTH) r2 = vpool.rows(sb[qd_v], off2);
+  };
+  const int vcol = vt_col(qd_v);
+  auto store_kv = [&](KVTile<D>& t) {
+    if constexpr (BOTH) {
+      store_k_rows<D>(t.k, r1, qd_k, cc_k);
+      store_vt_rows<D>(t.vt, r2, cc_v, vcol);
+    } else if (doK) {
+      store_k_rows<D>(t.k, r1, qd_k, cc_k);
+    } else {
+      store_vt_rows<D>(t.vt, r1, cc_v, vcol);
+    }
+  };
+  int* slot_words = reinterpret_cast<int*>(&slot_buf[0][0]);
+
+  if (nblk > 0) {
+    // ---- prologue: slots of blocks 0 and 1 into LDS, block 0 into LDS ----
+    BlockIter it_slot, it_comp;
+    iter_job(a, it_slot, jb);
+    it_comp = it_slot;
+    if (tid < 64) slot_words[tid] = block_slot(it_slot, tid);
+    iter_next(a, it_slot, je);
+    if (nblk > 1) {
+      if (tid < 64) slot_words[64 + tid] = block_slot(it_slot, tid);
+      iter_next(a, it_slot, je);
+    }
+    __syncthreads();
+    load_kv(slot_buf[0]);
+    store_kv(buf[0]);
+    __syncthreads();
+
+    int cur_job = -1, lim = 0;
+    bool wave_job = false;
+    for (int b = 0; b < nblk; ++b) {
+      // ---- issue the K/V loads of block b+1 and the page-table read of block b+2 ----
+      if (b + 1 < nblk) load_kv(slot_buf[(b + 1) & 1]);
+      int slot_after = 0;
+      const bool more = b + 2 < nblk;
+      if (more) {
+        if (tid < 64) slot_after = block_slot(it_slot, tid);
+        iter_next(a, it_slot, je);
+      }
+      // ---- compute block b ----
+      if (it_comp.j != cur_job) {
+        cur_job = it_comp.j;
+        const int32_t* job = a.jobs + (int64_t)cur_job * kJobWords;
+        const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+        lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+        wave_job = wave_live && __ballot(lim > job[1]) != 0;
+      }
+      const KVTile<D>& t = buf[b & 1];
+      if (wave_job) {
+        wave_block<D>(t, qreg, acc, m_run, l_run, lim - it_comp.kb, c2, li, hi);
+      }
+      // ---- block b+1 into the other buffer ----
+      if (b + 1 < nblk) store_kv(buf[(b + 1) & 1]);
+      if (more && tid < 64) slot_words[(b & 1) * 64 + tid] = slot_after;
+      iter_next(a, it_comp, je);
+      __syncthreads();
+    }
+  }
+
+  write_result<D>(a, tile, item, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
+}
+
+// ---------------------------------------------------------------------------
+// Wide bf16 extend kernel (head_dim 128): 8 waves, 256-row tiles.  Each K/V
+// block feeds twice the rows of the 4-wave kernel (half the loads, LDS stores
+// and barriers per flop), and each thread stages only one unit (waves 0-3 K,
+// waves 4-7 V), which leaves registers for two blocks of prefetch: at block
+// b the K/V rows of block b+2 are being loaded, block b+1 waits in registers,
+// and the page-table slots of block b+3 are read.
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 512;
+
+template <bool OFF32>
+__global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArgs a) {
+  constexpr int D = 128, KSTEPS = D / 16, DB = D / 32, CH = D / 8;
+  __shared__ KVTile<D> buf[2];
+  __shared__ int slot_ring[2][64];
+
+  const int tid = threadIdx.x;
+  const bool doK = tid < 256;
+  const int u = tid & 255;
+  const int qd = doK ? u / CH : u % 16;  // K units: chunk fastest; V units: key quad fastest
+  const int cc = doK ? u % CH : u / 16;
+
+  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
+  const int kvh = item[1];
+  const int jb = item[2], je = item[3];
+  const int tok_begin = tile[0], n_tok = tile[1];
+  const int group = a.group;
+  const int n_rows = n_tok * group;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int row = wave * 32 + li;
+  const int tloc = row / group;
+  int act_lo = 0, act_hi = n_tok;
+  if (tile[4] >= 0) {
+    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+    act_lo = cr0[0];
+    act_hi = cr0[1];
+  }
+  const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
+  const bool wave_live = __ballot(row_ok) != 0;
+
+  bf16x8 qreg[KSTEPS];
+  int qpos = 0;
+  if (row_ok) {
+    const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
+    qpos = tk[1];
+    const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
+                        ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qreg[s] = bf16x8{};
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  PoolReader<OFF32> pool;
+  pool.init(doK ? a.kp : a.vp, a.pool_bytes, (uint32_t)(a.hkv * D * 2));
+  const uint32_t off = (uint32_t)(kvh * D + 8 * cc) * 2;
+  const int vcol = vt_col(qd);
+
+  int nblk = 0;
+  for (int j = jb; j < je; ++j) {
+    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+    nblk += (job[2] - job[1] + 63) >> 6;
+  }
+
+  auto issue = [&](Rows4& r, const int* slots) {
+    const int4 sl = *reinterpret_cast<const int4*>(slots + 4 * qd);
+    r = pool.rows(sl, off);
+  };
+  auto stage = [&](KVTile<D>& t, const Rows4& r) {
+    if (doK)
+      store_k_rows<D>(t.k, r, qd, cc);
+    else
+      store_vt_rows<D>(t.vt, r, cc, vcol);
+  };
+
+  if (nblk > 0) {
+    BlockIter it_slot, it_comp;
+    iter_job(a, it_slot, jb);
+    it_comp = it_slot;
+    Rows4 rA, rB;
+    // ---- prologue: block 0 in LDS, block 1 in registers, slots of block 2 in the ring ----
+    if (tid < 64) slot_ring[0][tid] = block_slot(it_slot, tid);
+    iter_next(a, it_slot, je);
+    if (nblk > 1) {
+      if (tid < 64) slot_ring[1][tid] = block_slot(it_slot, tid);
+      iter_next(a, it_slot, je);
+    }
+    __syncthreads();
+    issue(rA, slot_ring[0]);
+    if (nblk > 1) issue(rB, slot_ring[1]);
+    __syncthreads();
+    if (nblk > 2) {
+      if (tid < 64) slot_ring[0][tid] = block_slot(it_slot, tid);
+      iter_next(a, it_slot, je);
+    }
+    stage(buf[0], rA);
+    __syncthreads();
+
+    int cur_job = -1, lim = 0;
+    bool wave_job = false;
+    // one key block: rcur holds nothing live (it is reloaded with block b+2),
+    // rnext holds block b+1 (staged into LDS after the compute)
+    auto step = [&](int b, Rows4& rcur, Rows4& rnext) {
+      if (b + 2 < nblk) issue(rcur, slot_ring[b & 1]);
+      int slot_after = 0;
+      const bool more = b + 3 < nblk;
+      if (more) {
+        if (tid < 64) slot_after = block_slot(it_slot, tid);
+        iter_next(a, it_slot, je);
+      }
+      if (it_comp.j != cur_job) {
+        cur_job = it_comp.j;
+        const int32_t* job = a.jobs + (int64_t)cur_job * kJobWords;
+        const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+        lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+        wave_job = wave_live && __ballot(lim > job[1]) != 0;
+      }
+      if (wave_job) wave_block<D>(buf[b & 1], qreg, acc, m_run, l_run, lim - it_comp.kb, c2, li, hi);
+      if (b + 1 < nblk) stage(buf[(b + 1) & 1], rnext);
+      if (more && tid < 64) slot_ring[(b + 1) & 1][tid] = slot_after;
+      iter_next(a, it_comp, je);
+      __syncthreads();
+    };
+    for (int b = 0; b < nblk; b += 2) {
+      step(b, rA, rB);
+      if (b + 1 < nblk) step(b + 1, rB, rA);
+    }
+  }
+  write_result<D>(a, tile, item, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (plain VALU, parity-grade).  One thread per query row of the
+// tile, scalar online softmax over the row's visible keys.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
+  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
+  const int kvh = item[1];
+  const int group = a.group;
+  const int n_rows = tile[1] * group;
+  const int row = threadIdx.x;
+  if (row >= n_rows) return;
+  const int tloc = row / group;
+  float q[D], acc[D];
+  float m_run = -INFINITY, l_run = 0.f;
+  const int32_t* tk = a.toks + (int64_t)(tile[0] + tloc) * kTokWords;
+  const int qpos = tk[1];
+  const float* src = reinterpret_cast<const float*>(a.q) + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D;
+  for (int d = 0; d < D; ++d) {
+    q[d] = src[d];
+    acc[d] = 0.f;
+  }
+  const float* kpool = reinterpret_cast<const float*>(a.kp);
+  const float* vpool = reinterpret_cast<const float*>(a.vp);
+  for (int j = item[2]; j < item[3]; ++j) {
+    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+    if (tloc < job[3] || tloc >= job[4]) continue;
+    const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
+    const int end = job[5] ? min(job[2], qpos + 1) : job[2];
+    for (int p = job[1]; p < end; ++p) {
+      const int64_t off = ((int64_t)prow[p] * a.hkv + kvh) * D;
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s = fmaf(q[d], kpool[off + d], s);
+      const float t = s * a.scale_log2;
+      const float m_new = fmaxf(m_run, t);
+      const float alpha = exp2f(m_run - m_new);
+      const float pw = exp2f(t - m_new);
+      l_run = l_run * alpha + pw;
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(pw, vpool[off + d], acc[d] * alpha);
+      m_run = m_new;
+    }
+  }
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (tile[4] < 0) {
+    float* dst = reinterpret_cast<float*>(a.o) + ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D;
+    for (int d = 0; d < D; ++d) dst[d] = acc[d] * inv;
+    return;
+  }
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+  if (tloc >= cr[0] && tloc < cr[1]) {
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+    for (int d = 0; d < D; ++d) a.ws_o[w * D + d] = acc[d] * inv;
+    a.ws_ml[w * 2] = m_run;
+    a.ws_ml[w * 2 + 1] = l_run;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KV scatter and page-table writes
+// ---------------------------------------------------------------------------
+__global__ void kv_store_kernel(uint4* __restrict__ kp, uint4* __restrict__ vp, const uint4* __restrict__ kn,
+                                const uint4* __restrict__ vn, const int32_t* __restrict__ slots, int64_t n,
+                                int64_t row_vecs) {
+  const int64_t total = n * row_vecs;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tok = i / row_vecs, e = i % row_vecs;
+    const int64_t dst = (int64_t)slots[tok] * row_vecs + e;
+    kp[dst] = kn[i];
+    vp[dst] = vn[i];
+  }
+}
+
+__global__ void page_table_write_kernel(int32_t* __restrict__ pt, int64_t ld, const int32_t* __restrict__ runs,
+                                        const int32_t* __restrict__ run_slots) {
+  const int32_t* r = runs + (int64_t)blockIdx.x * kRunWords;
+  int32_t* dst = pt + (int64_t)r[0] * ld + r[1];
+  const int32_t* src = run_slots + r[3];
+  for (int i = threadIdx.x; i < r[2]; i += blockDim.x) dst[i] = src[i];
+}
+
+}  // namespace rdx

@@ -83,7 +83,8 @@ _SIGS = {
     "rdx_extend_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
     "rdx_decode_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
     "rdx_timing_begin": (ctypes.c_int, [i32]),
-    "rdx_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), i32p, i32, i32p]),
+    "rdx_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), i32p, i32,
+                                       i32p]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -295,10 +296,13 @@ def timing_begin(cap: int):
 
 
 def timing_read(cap: int):
-    """-> (durations_ms np.float32[n], kinds np.int32[n]) of the launches recorded since timing_begin."""
+    """-> (attention_ms, merge_ms, kinds) of the launches recorded since
+    timing_begin: float32[n] kernel durations (merge 0 where none ran) and
+    int32[n] plan kinds, in launch order."""
     ms = np.zeros(max(cap, 1), np.float32)
+    mm = np.zeros(max(cap, 1), np.float32)
     kinds = np.zeros(max(cap, 1), np.int32)
     n = i32()
-    _check(lib().rdx_timing_read(ms.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _p32(kinds), cap,
-                                 ctypes.byref(n)))
-    return ms[: n.value].copy(), kinds[: n.value].copy()
+    fp = ctypes.POINTER(ctypes.c_float)
+    _check(lib().rdx_timing_read(ms.ctypes.data_as(fp), mm.ctypes.data_as(fp), _p32(kinds), cap, ctypes.byref(n)))
+    return ms[: n.value].copy(), mm[: n.value].copy(), kinds[: n.value].copy()
