@@ -47,6 +47,7 @@ extern "C" {
 #define RDX_ESTATE (-3)       /* unknown node, refcount underflow, slot not private */
 #define RDX_EUNSUPPORTED (-4) /* dtype / head_dim / head ratio not built */
 #define RDX_EDEVICE (-5)      /* a HIP call failed */
+#define RDX_ENOBUFS (-6)      /* a caller device buffer is too small (sizes reported) */
 
 const char* rdx_last_error(void);
 const char* rdx_version(void);
@@ -189,21 +190,24 @@ typedef struct rdx_plan_info {
   int64_t workspace_bytes;   /* attention workspace (0 when nothing is split) */
   int64_t new_slots_offset;  /* byte offset of the new-token slot list (int32[num_new]) */
   int64_t num_new;           /* = sum(q_len) */
-  int64_t num_items, num_tiles, num_jobs, num_split_tiles, num_shared_segments;
+  int64_t num_items;         /* workgroups of the launch: item records x Hkv */
+  int64_t num_tiles, num_jobs, num_split_tiles, num_shared_segments;
   int64_t key_rows;          /* sum over items of (tile rows x keys): work estimate */
 } rdx_plan_info;
 int rdx_plan_get_info(const rdx_plan* plan, rdx_plan_info* out);
 
 /* Copy the plan to dev_plan (device, >= device_bytes) on `stream` and write
  * the batch's page-table entries into page_table (device int32
- * [page_table_rows][ld]).  Reuses the plan's pinned staging buffer once the
- * previous upload has left it.  Errors: EINVAL, EDEVICE. */
+ * [page_table_rows][ld]).  The plan stages uploads through a ring of 4
+ * pinned host buffers; the call blocks only while the upload made 4 calls
+ * earlier has not left its buffer yet.  Errors: EINVAL, EDEVICE. */
 int rdx_plan_upload(rdx_plan* plan, void* dev_plan, int64_t dev_plan_bytes,
                     int32_t* page_table, int64_t page_table_rows, void* stream);
 
 /* Host view of a built plan (for tests and tools).  Arrays stay valid until
  * the next rdx_plan_build.  Record layouts are int32:
- *   item    [8] tile, kv_head, job_begin, job_end, contrib, 0, 0, 0
+ *   item    [4] tile, job_begin, job_end, contrib -- one per key chunk; the
+ *               launch runs item i for KV head h as workgroup i * Hkv + h
  *   tile    [8] tok_begin, n_tok, n_contrib, contrib_begin, counter (-1 = no merge), 0,0,0
  *   job     [8] page_row, key_begin, key_end, tok_lo, tok_hi, causal, 0, 0
  *   token   [2] q_index, position
@@ -241,6 +245,51 @@ int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const 
                          const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, void* o, void* workspace,
                          int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------- decode step */
+/* Caller-owned device buffers of one step. */
+typedef struct rdx_step_io {
+  void* dev_plan;            /* device plan buffer and its size in bytes */
+  int64_t dev_plan_bytes;
+  void* workspace;           /* attention workspace and its size in bytes */
+  int64_t workspace_bytes;
+  int32_t* page_table;       /* device int32 [page_table_rows][ld] */
+  int64_t page_table_rows;
+  void* k_pool;              /* device [num_slots][Hkv][head_dim] each */
+  void* v_pool;
+  const void* q;             /* device [num_reqs][Hq][head_dim] */
+  const void* k_new;         /* device [num_reqs][Hkv][head_dim] each */
+  const void* v_new;
+  void* o;                   /* device [num_reqs][Hq][head_dim] */
+} rdx_step_io;
+
+/* One decode step of a running batch in one call -- the serving loop's
+ * per-token path (SGLang explainer, RadixAttention section: slots come from
+ * the pool the cache shares, the page table maps positions to slots; BatchLLM
+ * explainer, Horizontal Fusion: shared prefixes are attended once per group).
+ * Every request gets one new token:
+ *   1. rdx_alloc(num_reqs) -> out_slots (slot i to request i);
+ *   2. host_page_table[row[i]][row_kv_len[row[i]]] = out_slots[i] and
+ *      row_kv_len[row[i]] += 1 (host arrays indexed by page-table row; the
+ *      host page table is int32 [num_rows][ld]);
+ *   3. plans the batch (rdx_plan_build with q_len 1 and written taken from
+ *      row_written), uploads it, writes the new page-table entries to the
+ *      device table and scatters k_new / v_new into the pools (one fused
+ *      kernel), then runs decode attention into o (RDX_PLAN_DECODE plan);
+ *   4. row_written[row[i]] = row_kv_len[row[i]].
+ * node[i]: the locked node of request i (as in rdx_batch).  out_info (may be
+ * NULL) receives the plan's sizes.  If io->dev_plan_bytes or
+ * io->workspace_bytes is too small the call returns RDX_ENOBUFS with the
+ * needed sizes in out_info, after returning the slots (the host arrays and
+ * the free set are as before; leaves evicted to make room stay evicted):
+ * grow the buffers and call again.  Other errors: EINVAL, ENOSPC, ESTATE,
+ * EUNSUPPORTED, EDEVICE, with the same rollback.  Device work is enqueued on
+ * `stream`; the call blocks only on the plan's staging ring (see
+ * rdx_plan_upload). */
+int rdx_decode_step(rdx_tree* tree, rdx_plan* plan, const rdx_attn_desc* desc, int32_t num_reqs,
+                    const int64_t* node, const int32_t* row, int32_t* row_kv_len, int32_t* row_written,
+                    int32_t* host_page_table, int64_t num_rows, int64_t ld, int32_t* out_slots,
+                    const rdx_step_io* io, void* stream, rdx_plan_info* out_info);
 
 /* ------------------------------------------------------- launch timing */
 /* For benchmarks.  rdx_timing_begin(cap) starts recording: the next (up to

@@ -371,7 +371,7 @@ __device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qr
 }
 
 // Final result of one lane's row: the normalised output (direct tiles) or
-// the partial state (split tiles, contribution item[4]).
+// the partial state (split tiles, contribution item[3]).
 template <int D>
 __device__ __forceinline__ void write_result(const AttnArgs& a, const int32_t* tile, const int32_t* item, int kvh,
                                              const f32x16 (&acc)[D / 32], float m_run, float l_run, bool row_ok,
@@ -396,7 +396,7 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const int32_t* t
     }
     return;
   }
-  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
   if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
     const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
     float* dst = a.ws_o + w * D;
@@ -441,10 +441,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int qd_v = uv % 16, cc_v = uv / 16;
   const int qd1 = doK ? qd_k : qd_v;  // the unit whose slots feed kr (head_dim 64: this thread's only unit)
 
-  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  // one item record per key chunk, run for every KV head: workgroup b takes
+  // record b / Hkv and KV head b % Hkv
+  const int32_t* item = a.items + (int64_t)(blockIdx.x / (unsigned)a.hkv) * kItemWords;
   const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
-  const int kvh = item[1];
-  const int jb = item[2], je = item[3];
+  const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
+  const int jb = item[1], je = item[2];
   const int tok_begin = tile[0], n_tok = tile[1];
   const int group = a.group;
   const int n_rows = n_tok * group;
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   // range of a split tile
   int act_lo = 0, act_hi = n_tok;
   if (tile[4] >= 0) {
-    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
     act_lo = cr0[0];
     act_hi = cr0[1];
   }
@@ -592,10 +594,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   const int qd = doK ? u / CH : u % 16;  // K units: chunk fastest; V units: key quad fastest
   const int cc = doK ? u % CH : u / 16;
 
-  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  // one item record per key chunk, run for every KV head: workgroup b takes
+  // record b / Hkv and KV head b % Hkv
+  const int32_t* item = a.items + (int64_t)(blockIdx.x / (unsigned)a.hkv) * kItemWords;
   const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
-  const int kvh = item[1];
-  const int jb = item[2], je = item[3];
+  const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
+  const int jb = item[1], je = item[2];
   const int tok_begin = tile[0], n_tok = tile[1];
   const int group = a.group;
   const int n_rows = n_tok * group;
@@ -605,7 +609,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   const int tloc = row / group;
   int act_lo = 0, act_hi = n_tok;
   if (tile[4] >= 0) {
-    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
     act_lo = cr0[0];
     act_hi = cr0[1];
   }
@@ -715,9 +719,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
-  const int32_t* item = a.items + (int64_t)blockIdx.x * kItemWords;
+  const int32_t* item = a.items + (int64_t)(blockIdx.x / (unsigned)a.hkv) * kItemWords;
   const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
-  const int kvh = item[1];
+  const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
   const int group = a.group;
   const int n_rows = tile[1] * group;
   const int row = threadIdx.x;
@@ -734,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   }
   const float* kpool = reinterpret_cast<const float*>(a.kp);
   const float* vpool = reinterpret_cast<const float*>(a.vp);
-  for (int j = item[2]; j < item[3]; ++j) {
+  for (int j = item[1]; j < item[2]; ++j) {
     const int32_t* job = a.jobs + (int64_t)j * kJobWords;
     if (tloc < job[3] || tloc >= job[4]) continue;
     const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
@@ -758,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
     for (int d = 0; d < D; ++d) dst[d] = acc[d] * inv;
     return;
   }
-  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[4]) * kContribWords;
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
   if (tloc >= cr[0] && tloc < cr[1]) {
     const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
     for (int d = 0; d < D; ++d) a.ws_o[w * D + d] = acc[d] * inv;
@@ -788,6 +792,30 @@ __global__ void page_table_write_kernel(int32_t* __restrict__ pt, int64_t ld, co
   int32_t* dst = pt + (int64_t)r[0] * ld + r[1];
   const int32_t* src = run_slots + r[3];
   for (int i = threadIdx.x; i < r[2]; i += blockDim.x) dst[i] = src[i];
+}
+
+// Page-table writes and KV scatter of one decode step in one launch:
+// workgroups [0, n_runs) each copy one page-table run, the others scatter
+// the new K/V rows (grid-stride over 16-byte vectors).
+__global__ void step_store_kernel(int32_t* __restrict__ pt, int64_t ld, const int32_t* __restrict__ runs,
+                                  const int32_t* __restrict__ run_slots, int32_t n_runs, uint4* __restrict__ kp,
+                                  uint4* __restrict__ vp, const uint4* __restrict__ kn, const uint4* __restrict__ vn,
+                                  const int32_t* __restrict__ slots, int64_t n, int64_t row_vecs) {
+  if ((int32_t)blockIdx.x < n_runs) {
+    const int32_t* r = runs + (int64_t)blockIdx.x * kRunWords;
+    int32_t* dst = pt + (int64_t)r[0] * ld + r[1];
+    const int32_t* src = run_slots + r[3];
+    for (int i = threadIdx.x; i < r[2]; i += blockDim.x) dst[i] = src[i];
+    return;
+  }
+  const int64_t total = n * row_vecs;
+  const int64_t nb = (int64_t)gridDim.x - n_runs;
+  for (int64_t i = ((int64_t)blockIdx.x - n_runs) * blockDim.x + threadIdx.x; i < total; i += nb * blockDim.x) {
+    const int64_t tok = i / row_vecs, e = i % row_vecs;
+    const int64_t dst = (int64_t)slots[tok] * row_vecs + e;
+    kp[dst] = kn[i];
+    vp[dst] = vn[i];
+  }
 }
 
 }  // namespace rdx

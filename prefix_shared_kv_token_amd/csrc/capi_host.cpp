@@ -7,11 +7,6 @@
 #include "plan.h"
 #include "radix_tree.h"
 
-struct rdx_tree {
-  rdx::RadixTree impl;
-  rdx_tree(int64_t n, int32_t u) : impl(n, u) {}
-};
-
 namespace rdx {
 std::string& last_error() {
   thread_local std::string msg;
@@ -133,16 +128,7 @@ int rdx_plan_get_info(const rdx_plan* plan, rdx_plan_info* out) {
   if (!plan || !out) return fail(RDX_EINVAL, "rdx_plan_get_info: null argument");
   auto* p = reinterpret_cast<const rdx::Plan*>(plan);
   if (!p->built) return fail(RDX_ESTATE, "rdx_plan_get_info: plan not built");
-  out->device_bytes = p->total_words * 4;
-  out->workspace_bytes = p->ws_bytes;
-  out->new_slots_offset = p->off_new * 4;
-  out->num_new = (int64_t)p->new_slots.size();
-  out->num_items = (int64_t)p->items.size() / rdx::kItemWords;
-  out->num_tiles = (int64_t)p->tiles.size() / rdx::kTileWords;
-  out->num_jobs = (int64_t)p->jobs.size() / rdx::kJobWords;
-  out->num_split_tiles = p->num_split_tiles;
-  out->num_shared_segments = p->num_shared_segments;
-  out->key_rows = p->key_rows;
+  p->fill_info(out);
   return rdx::ok();
 }
 

@@ -12,6 +12,7 @@
 #include "attn_kernels.h"
 #include "common.h"
 #include "plan.h"
+#include "radix_tree.h"
 
 
 using namespace rdx;
@@ -83,7 +84,8 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   if (!p->built) return fail(RDX_ESTATE, "attention: plan not built");
   if (p->kind != kind) return fail(RDX_EINVAL, "attention: plan kind %d does not match this entry point", p->kind);
   if (!same_shape(*desc, p->desc)) return fail(RDX_EINVAL, "attention: descriptor differs from the plan's");
-  const int64_t n_items = (int64_t)p->items.size() / kItemWords;
+  // workgroups: every item record once per KV head
+  const int64_t n_items = (int64_t)p->items.size() / kItemWords * desc->num_kv_heads;
   if (n_items == 0) return ok();
   if (!dev_plan || !q || !kp || !vp || !pt || !o) return fail(RDX_EINVAL, "attention: null device pointer");
   if (p->ws_bytes > 0 && (!ws || ws_bytes < p->ws_bytes))
@@ -144,6 +146,69 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   return ok();
 }
 
+// Plan upload: checks, staging through the plan's pinned ring, the H2D copy
+// and (write_pt) the page-table write kernel.
+int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_table, int64_t page_table_rows,
+                hipStream_t st, bool write_pt) {
+  if (!p->built) return fail(RDX_ESTATE, "rdx_plan_upload: plan not built");
+  const int64_t bytes = p->total_words * 4;
+  if (dev_plan_bytes < bytes) return fail(RDX_EINVAL, "rdx_plan_upload: device buffer of %lld bytes needed", (long long)bytes);
+  const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
+  if (n_runs > 0 && (!page_table || page_table_rows <= p->max_page_row))
+    return fail(RDX_EINVAL, "rdx_plan_upload: page table with more than %lld rows needed", (long long)p->max_page_row);
+  hipError_t e;
+  Plan::Stage& sg = p->stages[p->uploads % Plan::kStages];
+  if (!sg.event) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    sg.event = ev;
+  }
+  if (sg.pending) {
+    e = hipEventSynchronize(reinterpret_cast<hipEvent_t>(sg.event));
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    sg.pending = false;
+  }
+  if (sg.bytes < bytes) {
+    if (sg.pinned) hipHostFree(sg.pinned);
+    sg.pinned = nullptr;
+    sg.bytes = 0;
+    const int64_t want = bytes + bytes / 2 + 4096;
+    e = hipHostMalloc(&sg.pinned, want, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+    sg.bytes = want;
+  }
+  int32_t* h = reinterpret_cast<int32_t*>(sg.pinned);
+  auto put = [&](int64_t off, const std::vector<int32_t>& v) {
+    if (!v.empty()) memcpy(h + off, v.data(), v.size() * 4);
+  };
+  put(p->off_items, p->items);
+  put(p->off_tiles, p->tiles);
+  put(p->off_jobs, p->jobs);
+  put(p->off_toks, p->toks);
+  put(p->off_contribs, p->contribs);
+  put(p->off_runs, p->runs);
+  put(p->off_run_slots, p->run_slots);
+  put(p->off_new, p->new_slots);
+  put(p->off_cptr, p->cptr);
+  put(p->off_clist, p->clist);
+  put(p->off_mblocks, p->mblocks);
+  e = hipMemcpyAsync(dev_plan, sg.pinned, bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
+  if (write_pt && n_runs > 0) {
+    const int32_t* db = reinterpret_cast<const int32_t*>(dev_plan);
+    hipLaunchKernelGGL(page_table_write_kernel, dim3((unsigned)n_runs), dim3(256), 0, st, page_table, p->ld,
+                       db + p->off_runs, db + p->off_run_slots);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "page-table write launch");
+  }
+  e = hipEventRecord(reinterpret_cast<hipEvent_t>(sg.event), st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  sg.pending = true;
+  p->uploads++;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,71 +238,18 @@ int rdx_kv_store(const rdx_attn_desc* desc, void* k_pool, void* v_pool, const vo
 int rdx_plan_upload(rdx_plan* hplan, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_table,
                     int64_t page_table_rows, void* stream) {
   if (!hplan || !dev_plan) return fail(RDX_EINVAL, "rdx_plan_upload: null argument");
-  Plan* p = reinterpret_cast<Plan*>(hplan);
-  if (!p->built) return fail(RDX_ESTATE, "rdx_plan_upload: plan not built");
-  const int64_t bytes = p->total_words * 4;
-  if (dev_plan_bytes < bytes) return fail(RDX_EINVAL, "rdx_plan_upload: device buffer of %lld bytes needed", (long long)bytes);
-  const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
-  if (n_runs > 0 && (!page_table || page_table_rows <= p->max_page_row))
-    return fail(RDX_EINVAL, "rdx_plan_upload: page table with more than %lld rows needed", (long long)p->max_page_row);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (!p->event) {
-    hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-    p->event = ev;
-  }
-  if (p->upload_pending) {
-    e = hipEventSynchronize(reinterpret_cast<hipEvent_t>(p->event));
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-    p->upload_pending = false;
-  }
-  if (p->pinned_bytes < bytes) {
-    if (p->pinned) hipHostFree(p->pinned);
-    p->pinned = nullptr;
-    p->pinned_bytes = 0;
-    const int64_t want = bytes + bytes / 2 + 4096;
-    e = hipHostMalloc(&p->pinned, want, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
-    p->pinned_bytes = want;
-  }
-  int32_t* h = reinterpret_cast<int32_t*>(p->pinned);
-  auto put = [&](int64_t off, const std::vector<int32_t>& v) {
-    if (!v.empty()) memcpy(h + off, v.data(), v.size() * 4);
-  };
-  put(p->off_items, p->items);
-  put(p->off_tiles, p->tiles);
-  put(p->off_jobs, p->jobs);
-  put(p->off_toks, p->toks);
-  put(p->off_contribs, p->contribs);
-  put(p->off_runs, p->runs);
-  put(p->off_run_slots, p->run_slots);
-  put(p->off_new, p->new_slots);
-  put(p->off_cptr, p->cptr);
-  put(p->off_clist, p->clist);
-  put(p->off_mblocks, p->mblocks);
-  e = hipMemcpyAsync(dev_plan, p->pinned, bytes, hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
-  if (n_runs > 0) {
-    const int32_t* db = reinterpret_cast<const int32_t*>(dev_plan);
-    hipLaunchKernelGGL(page_table_write_kernel, dim3((unsigned)n_runs), dim3(256), 0, st, page_table, p->ld,
-                       db + p->off_runs, db + p->off_run_slots);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "page-table write launch");
-  }
-  e = hipEventRecord(reinterpret_cast<hipEvent_t>(p->event), st);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  p->upload_pending = true;
-  return ok();
+  return upload_plan(reinterpret_cast<Plan*>(hplan), dev_plan, dev_plan_bytes, page_table, page_table_rows,
+                     reinterpret_cast<hipStream_t>(stream), true);
 }
 
 void rdx_plan_destroy(rdx_plan* hplan) {
   if (!hplan) return;
   Plan* p = reinterpret_cast<Plan*>(hplan);
-  if (p->upload_pending && p->event) hipEventSynchronize(reinterpret_cast<hipEvent_t>(p->event));
-  if (p->event) hipEventDestroy(reinterpret_cast<hipEvent_t>(p->event));
-  if (p->pinned) hipHostFree(p->pinned);
+  for (Plan::Stage& sg : p->stages) {
+    if (sg.pending && sg.event) hipEventSynchronize(reinterpret_cast<hipEvent_t>(sg.event));
+    if (sg.event) hipEventDestroy(reinterpret_cast<hipEvent_t>(sg.event));
+    if (sg.pinned) hipHostFree(sg.pinned);
+  }
   delete p;
 }
 
@@ -253,6 +265,89 @@ int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const 
                          int64_t workspace_bytes, void* stream) {
   return launch_attention(desc, plan, RDX_PLAN_DECODE, dev_plan, q, k_pool, v_pool, page_table, o, workspace,
                           workspace_bytes, stream);
+}
+
+int rdx_decode_step(rdx_tree* tree, rdx_plan* hplan, const rdx_attn_desc* desc, int32_t num_reqs,
+                    const int64_t* node, const int32_t* row, int32_t* row_kv_len, int32_t* row_written,
+                    int32_t* host_page_table, int64_t num_rows, int64_t ld, int32_t* out_slots,
+                    const rdx_step_io* io, void* stream, rdx_plan_info* out_info) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!tree || !hplan || !io || num_reqs < 0 || num_rows <= 0 || ld <= 0)
+    return fail(RDX_EINVAL, "rdx_decode_step: bad arguments");
+  if (num_reqs > 0 && (!node || !row || !row_kv_len || !row_written || !host_page_table || !out_slots))
+    return fail(RDX_EINVAL, "rdx_decode_step: null array");
+  Plan* p = reinterpret_cast<Plan*>(hplan);
+  if (p->kind != RDX_PLAN_DECODE) return fail(RDX_EINVAL, "rdx_decode_step: not a decode plan");
+  if (!same_shape(*desc, p->desc)) return fail(RDX_EINVAL, "rdx_decode_step: descriptor differs from the plan's");
+  // per-request lengths in batch order (thread-local scratch: no allocation per step)
+  thread_local std::vector<int32_t> kv, wr, ql;
+  kv.resize(num_reqs);
+  wr.resize(num_reqs);
+  ql.assign(num_reqs, 1);
+  for (int32_t i = 0; i < num_reqs; ++i) {
+    const int32_t r = row[i];
+    if (r < 0 || r >= num_rows) return fail(RDX_EINVAL, "rdx_decode_step: request %d: row %d out of range", i, r);
+    if (row_kv_len[r] < 0 || row_kv_len[r] >= ld)
+      return fail(RDX_EINVAL, "rdx_decode_step: request %d: row %d is full", i, r);
+    kv[i] = row_kv_len[r] + 1;
+    wr[i] = row_written[r];
+  }
+  RadixTree& t = tree->impl;
+  rc = t.alloc(num_reqs, out_slots);
+  if (rc) return rc;
+  auto undo = [&](int code) {
+    // hand the slots back (the free set is as before the call); the error
+    // message of `code` is kept
+    std::string msg = last_error();
+    t.free_slots(out_slots, num_reqs);
+    last_error() = msg;
+    return code;
+  };
+  rdx_batch b{num_reqs, 0, node, row, kv.data(), ql.data(), wr.data(), out_slots};
+  p->ld = ld;
+  rc = p->build(t, b, ld);
+  if (rc) return undo(rc);
+  rdx_plan_info info;
+  p->fill_info(&info);
+  if (out_info) *out_info = info;
+  if (io->dev_plan_bytes < info.device_bytes || (info.workspace_bytes > 0 && io->workspace_bytes < info.workspace_bytes))
+    return undo(fail(RDX_ENOBUFS, "rdx_decode_step: buffers of %lld (plan) and %lld (workspace) bytes needed",
+                     (long long)info.device_bytes, (long long)info.workspace_bytes));
+  if (num_reqs > 0 && (!io->dev_plan || !io->page_table || !io->k_pool || !io->v_pool || !io->q || !io->k_new ||
+                       !io->v_new || !io->o))
+    return undo(fail(RDX_EINVAL, "rdx_decode_step: null device pointer"));
+  const int64_t esize = desc->dtype == RDX_BF16 ? 2 : 4;
+  const int64_t row_bytes = (int64_t)desc->num_kv_heads * desc->head_dim * esize;
+  if (row_bytes % 16) return undo(fail(RDX_EUNSUPPORTED, "rdx_decode_step: KV row of %lld bytes", (long long)row_bytes));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (num_reqs > 0) {
+    rc = upload_plan(p, io->dev_plan, io->dev_plan_bytes, io->page_table, io->page_table_rows, st, false);
+    if (rc) return undo(rc);
+    const int32_t* db = reinterpret_cast<const int32_t*>(io->dev_plan);
+    const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
+    const int64_t row_vecs = row_bytes / 16, total = (int64_t)num_reqs * row_vecs;
+    int64_t kv_blocks = (total + 255) / 256;
+    if (kv_blocks > 65536) kv_blocks = 65536;
+    hipLaunchKernelGGL(step_store_kernel, dim3((unsigned)(n_runs + kv_blocks)), dim3(256), 0, st, io->page_table, ld,
+                       db + p->off_runs, db + p->off_run_slots, (int32_t)n_runs,
+                       reinterpret_cast<uint4*>(io->k_pool), reinterpret_cast<uint4*>(io->v_pool),
+                       reinterpret_cast<const uint4*>(io->k_new), reinterpret_cast<const uint4*>(io->v_new),
+                       db + p->off_new, (int64_t)num_reqs, row_vecs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return undo(hip_fail(e, "step store launch"));
+    rc = launch_attention(desc, hplan, RDX_PLAN_DECODE, io->dev_plan, io->q, io->k_pool, io->v_pool, io->page_table,
+                          io->o, io->workspace, io->workspace_bytes, stream);
+    if (rc) return undo(rc);
+  }
+  // commit: the new slots into the host page-table rows, lengths, written counts
+  for (int32_t i = 0; i < num_reqs; ++i) {
+    const int32_t r = row[i];
+    host_page_table[(int64_t)r * ld + row_kv_len[r]] = out_slots[i];
+    row_kv_len[r] = kv[i];
+    row_written[r] = kv[i];
+  }
+  return ok();
 }
 
 int rdx_timing_begin(int32_t cap) {

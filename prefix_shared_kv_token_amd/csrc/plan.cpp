@@ -22,7 +22,7 @@
 #include "plan.h"
 
 #include <algorithm>
-#include <unordered_map>
+#include <atomic>
 
 #include "common.h"
 
@@ -34,15 +34,39 @@ int64_t align16(int64_t w) { return (w + 15) & ~int64_t(15); }
 
 struct Seg {
   int64_t start, end;  // key positions
-  int rep = -1;        // request whose page-table row is read for this segment
+  int rep;             // request whose page-table row is read for this segment
 };
 
 struct Req {
   int32_t row, kv_len, q_len, written, q_off, depth, shared_len;
   int64_t new_off;
-  std::vector<const Node*> path;
-  std::vector<int> segs;  // shared segment ids, top-down
+  int32_t path_off, path_len;  // its root-to-node path in path_buf
+  int32_t seg_off, seg_len;    // its shared segment ids (top-down) in seg_buf
 };
+
+struct TileReq {
+  int r, lo, hi;  // request, its tile-local token range
+};
+
+struct Job {
+  int32_t row, k0, k1, lo, hi, causal;
+};
+
+// Build scratch, reused across builds on a thread so a decode step does not
+// allocate.
+struct Scratch {
+  std::vector<Req> rq;
+  std::vector<const Node*> path_buf;
+  std::vector<int> seg_buf, order, seen, tile_tr_begin, tile_job_begin;
+  std::vector<Seg> segs;
+  std::vector<TileReq> trs;
+  std::vector<Job> tjobs, shared;
+  std::vector<int32_t> row_set;  // open addressing: request index, -1 empty
+};
+thread_local Scratch g_scratch;
+std::atomic<int64_t> g_epoch{0};
+
+uint32_t hash_row(int32_t row) { return (uint32_t)row * 2654435761u; }
 
 }  // namespace
 
@@ -52,9 +76,16 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     return fail(RDX_EINVAL, "rdx_plan_build: bad batch pointers");
   if (page_ld <= 0 || page_ld > (int64_t)1 << 30) return fail(RDX_EINVAL, "rdx_plan_build: bad page-table stride");
   const int R = b.num_reqs;
-  std::vector<Req> rq(R);
+  Scratch& sc = g_scratch;
+  const int64_t ep = ++g_epoch;
+  std::vector<Req>& rq = sc.rq;
+  rq.resize(R);
+  sc.path_buf.clear();
+  // duplicate page-table rows: open-addressing set of request indices
+  uint32_t cap = 16;
+  while (cap < 2u * (uint32_t)R) cap <<= 1;
+  sc.row_set.assign(cap, -1);
   int64_t total_new = 0;
-  std::unordered_map<int32_t, int> row_seen;
   max_page_row = -1;
   for (int r = 0; r < R; ++r) {
     Req& q = rq[r];
@@ -66,8 +97,18 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     q.new_off = total_new;
     const Node* n = tree.find(b.node[r]);
     if (!n) return fail(RDX_ESTATE, "rdx_plan_build: request %d: unknown node %lld", r, (long long)b.node[r]);
-    for (const Node* p = n; p != tree.root(); p = p->parent) q.path.push_back(p);
-    std::reverse(q.path.begin(), q.path.end());
+    q.path_off = (int32_t)sc.path_buf.size();
+    for (const Node* p = n; p != tree.root(); p = p->parent) {
+      sc.path_buf.push_back(p);
+      if (p->plan_epoch != ep) {
+        p->plan_epoch = ep;
+        p->plan_count = 0;
+        p->plan_seg = -1;
+      }
+      p->plan_count++;
+    }
+    q.path_len = (int32_t)sc.path_buf.size() - q.path_off;
+    std::reverse(sc.path_buf.begin() + q.path_off, sc.path_buf.end());
     q.depth = n == tree.root() ? 0 : (int32_t)n->end();
     const int64_t first_new = (int64_t)q.kv_len - q.q_len;
     if (q.row < 0 || q.q_len < 0 || q.q_len > q.kv_len || q.kv_len > page_ld || q.depth > first_new ||
@@ -75,8 +116,15 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
       return fail(RDX_EINVAL,
                   "rdx_plan_build: request %d inconsistent (row %d kv_len %d q_len %d written %d cached %d)", r,
                   q.row, q.kv_len, q.q_len, q.written, q.depth);
-    if (!row_seen.emplace(q.row, r).second)
-      return fail(RDX_EINVAL, "rdx_plan_build: requests %d and %d share page-table row %d", row_seen[q.row], r, q.row);
+    for (uint32_t h = hash_row(q.row) & (cap - 1);; h = (h + 1) & (cap - 1)) {
+      const int32_t o = sc.row_set[h];
+      if (o < 0) {
+        sc.row_set[h] = r;
+        break;
+      }
+      if (rq[o].row == q.row)
+        return fail(RDX_EINVAL, "rdx_plan_build: requests %d and %d share page-table row %d", o, r, q.row);
+    }
     max_page_row = std::max<int64_t>(max_page_row, q.row);
     total_new += q.q_len;
     if (total_new > ((int64_t)1 << 30)) return fail(RDX_EINVAL, "rdx_plan_build: too many new tokens");
@@ -87,39 +135,48 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
       return fail(RDX_EINVAL, "rdx_plan_build: new slot %d out of range", b.new_slots[i]);
 
   // ---- sharing: nodes reached by >= 2 requests, grouped into segments ----
-  std::unordered_map<const Node*, int> cnt;
-  for (auto& q : rq)
-    for (const Node* n : q.path) cnt[n]++;
-  std::unordered_map<const Node*, int> seg_of_first;
-  std::vector<Seg> segs;
+  std::vector<Seg>& segs = sc.segs;
+  segs.clear();
+  sc.seg_buf.clear();
   for (auto& q : rq) {
-    size_t i = 0;
-    while (i < q.path.size() && cnt[q.path[i]] >= 2) {
-      size_t j = i;
-      while (j + 1 < q.path.size() && cnt[q.path[j + 1]] == cnt[q.path[i]]) ++j;
-      auto it = seg_of_first.find(q.path[i]);
-      int s;
-      if (it == seg_of_first.end()) {
+    const Node* const* path = sc.path_buf.data() + q.path_off;
+    q.seg_off = (int32_t)sc.seg_buf.size();
+    int i = 0;
+    while (i < q.path_len && path[i]->plan_count >= 2) {
+      int j = i;
+      while (j + 1 < q.path_len && path[j + 1]->plan_count == path[i]->plan_count) ++j;
+      int s = path[i]->plan_seg;
+      if (s < 0) {
         s = (int)segs.size();
-        segs.push_back({q.path[i]->start, q.path[j]->end(), -1});
-        seg_of_first.emplace(q.path[i], s);
-      } else {
-        s = it->second;
+        segs.push_back({path[i]->start, path[j]->end(), -1});
+        path[i]->plan_seg = s;
       }
-      q.segs.push_back(s);
+      sc.seg_buf.push_back(s);
       i = j + 1;
     }
-    q.shared_len = q.segs.empty() ? 0 : (int32_t)segs[q.segs.back()].end;
+    q.seg_len = (int32_t)sc.seg_buf.size() - q.seg_off;
+    q.shared_len = q.seg_len == 0 ? 0 : (int32_t)segs[sc.seg_buf[q.seg_off + q.seg_len - 1]].end;
   }
   num_shared_segments = (int64_t)segs.size();
 
   // ---- depth-first order: lexicographic on segment lists (stable) ----
-  std::vector<int> order(R);
+  std::vector<int>& order = sc.order;
+  order.resize(R);
   for (int r = 0; r < R; ++r) order[r] = r;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int c) { return rq[a].segs < rq[c].segs; });
+  const int* sb = sc.seg_buf.data();
+  auto seg_less = [&](int a, int c) {
+    const Req& x = rq[a];
+    const Req& y = rq[c];
+    return std::lexicographical_compare(sb + x.seg_off, sb + x.seg_off + x.seg_len, sb + y.seg_off,
+                                        sb + y.seg_off + y.seg_len);
+  };
+  // batches usually arrive grouped already (admission order)
+  if (!std::is_sorted(order.begin(), order.end(), seg_less)) std::stable_sort(order.begin(), order.end(), seg_less);
   for (int r : order)
-    for (int s : rq[r].segs)
-      if (segs[s].rep < 0) segs[s].rep = r;
+    for (int k = 0; k < rq[r].seg_len; ++k) {
+      Seg& sg = segs[sb[rq[r].seg_off + k]];
+      if (sg.rep < 0) sg.rep = r;
+    }
 
   // ---- page-table writes: [written, kv_len) of each row ----
   runs.clear();
@@ -128,7 +185,9 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     const Req& q = rq[r];
     if (q.written >= q.kv_len) continue;
     int64_t src = (int64_t)run_slots.size();
-    for (const Node* n : q.path) {
+    const Node* const* path = sc.path_buf.data() + q.path_off;
+    for (int k = 0; k < q.path_len; ++k) {
+      const Node* n = path[k];
       for (int64_t p = std::max<int64_t>(n->start, q.written); p < n->end(); ++p)
         run_slots.push_back(n->slots[p - n->start]);
     }
@@ -144,67 +203,72 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   const int tt = tile_tokens();
   toks.clear();
   tiles.clear();
-  struct TileReq { int r, lo, hi; };
-  std::vector<std::vector<TileReq>> tile_reqs;
+  sc.trs.clear();
+  sc.tile_tr_begin.clear();
   int64_t cur_key = INT64_MIN;
   for (int r : order) {
     const Req& q = rq[r];
     if (q.q_len == 0) continue;
     int64_t key;
     if (kind == RDX_PLAN_EXTEND)
-      key = q.segs.empty() ? -1 - (int64_t)r : q.segs.back();
+      key = q.seg_len == 0 ? -1 - (int64_t)r : sb[q.seg_off + q.seg_len - 1];
     else
-      key = q.segs.empty() ? -1 : q.segs.front();
+      key = q.seg_len == 0 ? -1 : sb[q.seg_off];
     for (int t = 0; t < q.q_len; ++t) {
-      int ntile = (int)tile_reqs.size();
+      int ntile = (int)sc.tile_tr_begin.size();
       bool fresh = ntile == 0 || key != cur_key || tiles[(ntile - 1) * kTileWords + 1] >= tt;
       if (fresh) {
         tiles.insert(tiles.end(), {(int32_t)(toks.size() / kTokWords), 0, 0, 0, -1, 0, 0, 0});
-        tile_reqs.emplace_back();
+        sc.tile_tr_begin.push_back((int)sc.trs.size());
         cur_key = key;
         ntile++;
       }
       int32_t* tl = &tiles[(ntile - 1) * kTileWords];
-      auto& trs = tile_reqs.back();
       int local = tl[1];
-      if (trs.empty() || trs.back().r != r) trs.push_back({r, local, local});
-      trs.back().hi = local + 1;
+      if ((int)sc.trs.size() == sc.tile_tr_begin.back() || sc.trs.back().r != r) sc.trs.push_back({r, local, local});
+      sc.trs.back().hi = local + 1;
       tl[1]++;
       toks.push_back(q.q_off + t);
       toks.push_back(q.kv_len - q.q_len + t);
     }
   }
-  const int ntiles = (int)tile_reqs.size();
+  const int ntiles = (int)sc.tile_tr_begin.size();
+  sc.tile_tr_begin.push_back((int)sc.trs.size());
 
-  // ---- jobs per tile (before splitting) ----
-  struct Job { int32_t row, k0, k1, lo, hi, causal; };
-  std::vector<std::vector<Job>> tile_jobs(ntiles);
+  // ---- jobs per tile (before splitting): its shared segments, then each
+  // request's own causal range ----
+  sc.tjobs.clear();
+  sc.tile_job_begin.clear();
   int64_t total_cost = 0;
   for (int t = 0; t < ntiles; ++t) {
-    auto& trs = tile_reqs[t];
-    std::vector<int> seen;
-    std::vector<Job> shared;
-    for (auto& tr : trs) {
-      for (int s : rq[tr.r].segs) {
-        auto it = std::find(seen.begin(), seen.end(), s);
-        if (it == seen.end()) {
-          seen.push_back(s);
-          shared.push_back({rq[segs[s].rep].row, (int32_t)segs[s].start, (int32_t)segs[s].end, tr.lo, tr.hi, 0});
+    sc.tile_job_begin.push_back((int)sc.tjobs.size());
+    sc.seen.clear();
+    sc.shared.clear();
+    for (int k = sc.tile_tr_begin[t]; k < sc.tile_tr_begin[t + 1]; ++k) {
+      const TileReq& tr = sc.trs[k];
+      const Req& q = rq[tr.r];
+      for (int m = 0; m < q.seg_len; ++m) {
+        const int s = sb[q.seg_off + m];
+        auto it = std::find(sc.seen.begin(), sc.seen.end(), s);
+        if (it == sc.seen.end()) {
+          sc.seen.push_back(s);
+          sc.shared.push_back({rq[segs[s].rep].row, (int32_t)segs[s].start, (int32_t)segs[s].end, tr.lo, tr.hi, 0});
         } else {
-          Job& j = shared[it - seen.begin()];
+          Job& j = sc.shared[it - sc.seen.begin()];
           j.lo = std::min(j.lo, tr.lo);
           j.hi = std::max(j.hi, tr.hi);
         }
       }
     }
-    auto& js = tile_jobs[t];
-    js = shared;
-    for (auto& tr : trs) {
+    sc.tjobs.insert(sc.tjobs.end(), sc.shared.begin(), sc.shared.end());
+    for (int k = sc.tile_tr_begin[t]; k < sc.tile_tr_begin[t + 1]; ++k) {
+      const TileReq& tr = sc.trs[k];
       const Req& q = rq[tr.r];
-      if (q.kv_len > q.shared_len) js.push_back({q.row, q.shared_len, q.kv_len, tr.lo, tr.hi, 1});
+      if (q.kv_len > q.shared_len) sc.tjobs.push_back({q.row, q.shared_len, q.kv_len, tr.lo, tr.hi, 1});
     }
-    for (auto& j : js) total_cost += j.k1 - j.k0;
   }
+  sc.tile_job_begin.push_back((int)sc.tjobs.size());
+  for (const Job& j : sc.tjobs) total_cost += j.k1 - j.k0;
 
   // ---- split into items ----
   const int hkv = desc.num_kv_heads;
@@ -228,12 +292,14 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   ws_tokens = 0;
   key_rows = 0;
   struct ItemRec { int32_t tile, jb, je, c; int64_t cost; };
-  std::vector<ItemRec> its;
+  static thread_local std::vector<ItemRec> its, mine;
+  its.clear();
   for (int t = 0; t < ntiles; ++t) {
     int32_t* tl = &tiles[t * kTileWords];
-    std::vector<ItemRec> mine;
+    mine.clear();
     int64_t cur = 0;
-    for (const Job& j : tile_jobs[t]) {
+    for (int jx = sc.tile_job_begin[t]; jx < sc.tile_job_begin[t + 1]; ++jx) {
+      const Job& j = sc.tjobs[jx];
       for (int64_t a = j.k0; a < j.k1;) {
         int64_t room = chunk - cur;
         if (room <= 0 || mine.empty()) {
@@ -285,8 +351,9 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   key_rows *= hkv;
   // longest items first (all KV heads of an item next to each other)
   std::stable_sort(its.begin(), its.end(), [](const ItemRec& a, const ItemRec& c) { return a.cost > c.cost; });
-  for (auto& it : its)
-    for (int h = 0; h < hkv; ++h) items.insert(items.end(), {it.tile, h, it.jb, it.je, it.c, 0, 0, 0});
+  // one record per chunk; the launch runs record i for KV heads 0..Hkv-1 as
+  // workgroups i*Hkv .. i*Hkv+Hkv-1
+  for (auto& it : its) items.insert(items.end(), {it.tile, it.jb, it.je, it.c});
 
   // ---- workspace ----
   const int64_t hq = desc.num_q_heads, d = desc.head_dim;
@@ -296,6 +363,19 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   layout();
   built = true;
   return ok();
+}
+
+void Plan::fill_info(rdx_plan_info* out) const {
+  out->device_bytes = total_words * 4;
+  out->workspace_bytes = ws_bytes;
+  out->new_slots_offset = off_new * 4;
+  out->num_new = (int64_t)new_slots.size();
+  out->num_items = (int64_t)items.size() / kItemWords * desc.num_kv_heads;
+  out->num_tiles = (int64_t)tiles.size() / kTileWords;
+  out->num_jobs = (int64_t)jobs.size() / kJobWords;
+  out->num_split_tiles = num_split_tiles;
+  out->num_shared_segments = num_shared_segments;
+  out->key_rows = key_rows;
 }
 
 void Plan::layout() {

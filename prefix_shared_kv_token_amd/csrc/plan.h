@@ -20,7 +20,7 @@ constexpr int kTileRows = 128;   // query rows (token x grouped head) per tile
 constexpr int kKeyBlock = 64;    // keys per inner iteration of the kernels
 
 // Record layouts (int32 words) -- shared with the device code.
-constexpr int kItemWords = 8;     // tile, kv_head, job_begin, job_end, contrib
+constexpr int kItemWords = 4;     // tile, job_begin, job_end, contrib (one per key chunk; run for every KV head)
 constexpr int kTileWords = 8;     // tok_begin, n_tok, n_contrib, contrib_begin, split index (-1: none), cptr base
 constexpr int kJobWords = 8;      // page_row, key_begin, key_end, tok_lo, tok_hi, causal
 constexpr int kTokWords = 2;      // q_index, position
@@ -46,11 +46,17 @@ struct Plan {
           total_words = 0;
   int64_t ws_ml_offset = 0, ws_bytes = 0;
   bool built = false;
-  // upload staging (pinned host memory + completion event), owned by the plan
-  void* pinned = nullptr;
-  int64_t pinned_bytes = 0;
-  void* event = nullptr;
-  bool upload_pending = false;
+  // upload staging, owned by the plan: a ring of pinned host buffers, each
+  // with the event of the last copy out of it, so the host can prepare the
+  // next uploads while earlier ones are still queued
+  static constexpr int kStages = 4;
+  struct Stage {
+    void* pinned = nullptr;
+    int64_t bytes = 0;
+    void* event = nullptr;
+    bool pending = false;
+  } stages[kStages];
+  int64_t uploads = 0;
 
   // query rows per tile: 256 for the wide bf16 head_dim-128 extend kernel,
   // kTileRows otherwise
@@ -59,6 +65,7 @@ struct Plan {
   int tile_tokens() const { return tile_rows / group(); }
   int build(const RadixTree& tree, const rdx_batch& b, int64_t ld);
   void layout();
+  void fill_info(rdx_plan_info* out) const;
 };
 
 }  // namespace rdx

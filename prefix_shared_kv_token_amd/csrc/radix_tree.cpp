@@ -22,10 +22,9 @@
 namespace rdx {
 
 RadixTree::RadixTree(int64_t num_slots, int32_t match_unit)
-    : num_slots_(num_slots), unit_(match_unit), state_(num_slots, kFree) {
-  std::vector<int32_t> all(num_slots);
-  for (int64_t i = 0; i < num_slots; ++i) all[i] = (int32_t)i;
-  free_heap_ = decltype(free_heap_)(std::greater<int32_t>(), std::move(all));
+    : num_slots_(num_slots), unit_(match_unit), state_(num_slots, kFree),
+      free_bits_((num_slots + 63) / 64, ~uint64_t(0)), n_free_(num_slots) {
+  if (num_slots % 64) free_bits_.back() = (uint64_t(1) << (num_slots % 64)) - 1;
 }
 
 RadixTree::~RadixTree() = default;
@@ -180,7 +179,7 @@ int64_t RadixTree::evict_until(int64_t free_target, int64_t min_freed) {
     parent->children.erase(v->key[0]);
     for (int32_t s : v->slots) {
       state_[s] = kFree;
-      free_heap_.push(s);
+      release(s);
     }
     freed += (int64_t)v->key.size();
     evictions_++;
@@ -201,12 +200,22 @@ int RadixTree::alloc(int64_t n, int32_t* out) {
     evict_until(n, 0);
     if (num_free() < n) return fail(RDX_ESTATE, "rdx_alloc: eviction fell short (inconsistent reference counts)");
   }
-  for (int64_t i = 0; i < n; ++i) {
-    int32_t s = free_heap_.top();
-    free_heap_.pop();
-    state_[s] = kPrivate;
-    out[i] = s;
+  // the n smallest free ids, ascending
+  int64_t i = 0, w = low_word_;
+  while (i < n) {
+    uint64_t bits = free_bits_[w];
+    while (bits && i < n) {
+      const int b = __builtin_ctzll(bits);
+      bits &= bits - 1;
+      const int32_t s = (int32_t)(w * 64 + b);
+      state_[s] = kPrivate;
+      out[i++] = s;
+    }
+    free_bits_[w] = bits;
+    if (!bits) ++w;
   }
+  low_word_ = w;
+  n_free_ -= n;
   return ok();
 }
 
@@ -216,7 +225,7 @@ int RadixTree::free_slots(const int32_t* slots, int64_t n) {
   if (rc) return rc;
   for (int64_t i = 0; i < n; ++i) {
     state_[slots[i]] = kFree;
-    free_heap_.push(slots[i]);
+    release(slots[i]);
   }
   return ok();
 }

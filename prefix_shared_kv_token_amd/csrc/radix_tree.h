@@ -26,6 +26,11 @@ struct Node {
   int64_t last_access = 0;
   int64_t ref = 0;
   int64_t end() const { return start + (int64_t)key.size(); }
+  // batch-planner scratch: meaningful only while plan_epoch equals the epoch
+  // of the build that is running (builds on one tree are never concurrent)
+  mutable int64_t plan_epoch = 0;
+  mutable int32_t plan_count = 0;  // requests of the batch whose path holds this node
+  mutable int32_t plan_seg = -1;   // shared segment starting at this node
 };
 
 class RadixTree {
@@ -44,7 +49,7 @@ class RadixTree {
   int evict(int64_t n_tokens, int64_t* out_freed);
 
   int64_t num_slots() const { return num_slots_; }
-  int64_t num_free() const { return (int64_t)free_heap_.size(); }
+  int64_t num_free() const { return n_free_; }
   int64_t num_nodes() const { return (int64_t)nodes_.size(); }
   int64_t evictions() const { return evictions_; }
   int64_t clock() const { return clock_; }
@@ -80,7 +85,23 @@ class RadixTree {
   int64_t clock_ = 0;
   int64_t evictions_ = 0;
   std::vector<uint8_t> state_;
-  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_heap_;
+  // free set as a bitmap (bit s set <=> slot s free); every word below
+  // low_word_ is fully allocated, so the smallest free ids are found by a
+  // forward scan from there
+  std::vector<uint64_t> free_bits_;
+  int64_t n_free_ = 0;
+  int64_t low_word_ = 0;
+  void release(int32_t s) {
+    free_bits_[s >> 6] |= uint64_t(1) << (s & 63);
+    n_free_++;
+    if ((s >> 6) < low_word_) low_word_ = s >> 6;
+  }
 };
 
 }  // namespace rdx
+
+// The C ABI's opaque tree handle.
+struct rdx_tree {
+  rdx::RadixTree impl;
+  rdx_tree(int64_t n, int32_t u) : impl(n, u) {}
+};

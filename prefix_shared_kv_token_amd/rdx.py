@@ -17,7 +17,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librdx.so")
 
-OK, EINVAL, ENOSPC, ESTATE, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ENOSPC, ESTATE, EUNSUPPORTED, EDEVICE, ENOBUFS = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 PLAN_EXTEND, PLAN_DECODE = 0, 1
 
@@ -59,6 +59,12 @@ class PlanView(ctypes.Structure):
                 ("contribs", i32p), ("num_contribs", i64), ("tile_rows", i32), ("group", i32)]
 
 
+class StepIO(ctypes.Structure):
+    _fields_ = [("dev_plan", vp), ("dev_plan_bytes", i64), ("workspace", vp), ("workspace_bytes", i64),
+                ("page_table", vp), ("page_table_rows", i64), ("k_pool", vp), ("v_pool", vp),
+                ("q", vp), ("k_new", vp), ("v_new", vp), ("o", vp)]
+
+
 _SIGS = {
     "rdx_last_error": (ctypes.c_char_p, []),
     "rdx_version": (ctypes.c_char_p, []),
@@ -82,6 +88,8 @@ _SIGS = {
     "rdx_plan_upload": (ctypes.c_int, [vp, vp, i64, vp, i64, vp]),
     "rdx_extend_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
     "rdx_decode_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+    "rdx_decode_step": (ctypes.c_int, [vp, vp, ctypes.POINTER(AttnDesc), i32, i64p, i32p, i32p, i32p, i32p, i64,
+                                       i64, i32p, ctypes.POINTER(StepIO), vp, ctypes.POINTER(PlanInfo)]),
     "rdx_timing_begin": (ctypes.c_int, [i32]),
     "rdx_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), i32p, i32,
                                        i32p]),
@@ -262,7 +270,7 @@ class Plan:
                 return np.zeros((0, w), np.int32)
             return np.ctypeslib.as_array(p, shape=(n * w,)).reshape(n, w).copy()
 
-        return dict(items=arr(v.items, v.num_items, 8), tiles=arr(v.tiles, v.num_tiles, 8),
+        return dict(items=arr(v.items, v.num_items, 4), tiles=arr(v.tiles, v.num_tiles, 8),
                     jobs=arr(v.jobs, v.num_jobs, 8), tokens=arr(v.tokens, v.num_tokens, 2),
                     contribs=arr(v.contribs, v.num_contribs, 4), tile_rows=v.tile_rows, group=v.group)
 

@@ -134,6 +134,26 @@ def test_deterministic_and_kv_store_roundtrip():
     np.testing.assert_array_equal(vp, v_log)
 
 
+def test_separate_calls_match_decode_step():
+    """The decode path through the separate entry points (rdx_plan_build,
+    rdx_plan_upload, rdx_kv_store, rdx_decode_attention; used when launches
+    are recorded) gives bit-identical outputs to rdx_decode_step."""
+    torch = _torch()
+    from prefix_shared_kv_token_amd.driver import WorkloadRun
+
+    cfg = config_by_name("multilevel").replace(levels=((1, 90), (2, 40), (3, 13)), decode_steps=5)
+    run = WorkloadRun(Workload(cfg))
+    a = run.run()
+    b = run.run(record=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a["extend"], b["extend"]):
+        assert torch.equal(x, y)
+    assert torch.equal(a["decode"], b["decode"])
+    for p, q in zip(a["rows"], b["rows"]):
+        for x, y in zip(p, q):
+            np.testing.assert_array_equal(x, y)
+
+
 @pytest.mark.parametrize("cfg", CONFIGS[1:], ids=lambda c: c.name)
 def test_full_size_sampled(cfg):
     """Full-size workloads, default launch configuration (as timed by the

@@ -49,13 +49,11 @@ def _check_coverage(plan, kv_len, q_len, rows, hkv):
         for j in range(t[0], t[0] + t[1]):
             seen_tok[toks[j, 0]] += 1
     assert (seen_tok == 1).all()
-    for it in items:
+    for it, kvh in ((it, h) for it in items for h in range(hkv)):
         tile = tiles[it[0]]
-        kvh = it[1]
-        assert 0 <= kvh < hkv
         if tile[2] > 1:
-            c = contribs[tile[3] + it[4]]
-        for jb in range(it[2], it[3]):
+            c = contribs[tile[3] + it[3]]
+        for jb in range(it[1], it[2]):
             j = jobs[jb]
             for tl in range(j[3], j[4]):
                 qi, pos = toks[tile[0] + tl]
