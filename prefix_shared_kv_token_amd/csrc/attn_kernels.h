@@ -573,6 +573,317 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 decode kernel: tiles of at most 64 query rows (decode tiles are a
+// sharing group's new tokens x the GQA group, which fit), one workgroup per
+// work item.  Memory-bound by design, so it is built to keep many bytes in
+// flight: each thread stages 1/256 of a 64-key K and V block (4 threads per
+// key row) and two blocks are in flight in registers while a third is being
+// computed from LDS.  Wave w owns rows 16w..16w+15 and uses the 16x16x32 bf16
+// MFMA: S^T = K Q^T (K read row-major from LDS), then O^T = V^T P^T with V^T
+// fragments from the gfx950 transposing LDS read (ds_read_b64_tr_b16) of the
+// row-major V block; P^T is the score accumulator repacked to bf16 in place,
+// with the keys of each 32-key step taken in the order the accumulators hold
+// them (lane group g: keys 4g..4g+3 of the first 16, then of the second).
+// Keys past a job's end and blocks past the item's end are loaded through
+// out-of-range buffer offsets, which return zeros without touching memory.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct DecTile {
+  static constexpr int KS = D + 8;   // K row stride (elements): conflict-free 16-byte fragment reads
+  static constexpr int VS = D + 16;  // V row stride: conflict-free transposing reads
+  __bf16 k[64 * KS];
+  __bf16 v[64 * VS];
+};
+
+// max / sum of x over lanes l and l ^ 16 (gfx950 row swap, no LDS)
+__device__ __forceinline__ float row16_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row16_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+constexpr uint32_t kNoRow = 0x80000000u;  // buffer offset past any pool this path addresses
+
+// One thread's share of a K/V block: CPT 16-byte chunks of one key row of K
+// and of V.
+template <int CPT>
+struct DecStage {
+  uint4 k[CPT], v[CPT];
+};
+
+template <int D, bool OFF32>
+struct DecPool {
+  __amdgpu_buffer_rsrc_t kr, vr;
+  const char *kb, *vb;
+  uint32_t row_bytes;
+  __device__ void init(const AttnArgs& a) {
+    row_bytes = (uint32_t)(a.hkv * D * 2);
+    kb = reinterpret_cast<const char*>(a.kp);
+    vb = reinterpret_cast<const char*>(a.vp);
+    if constexpr (OFF32) {
+      kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kp), (short)0, (int)a.pool_bytes, 0x00020000);
+      vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.vp), (short)0, (int)a.pool_bytes, 0x00020000);
+    }
+  }
+  // byte offset of this thread's first chunk for `slot` (< 0: no row)
+  __device__ __forceinline__ uint32_t offset(int slot, uint32_t in_row) const {
+    if constexpr (OFF32) return slot >= 0 ? __umul24((uint32_t)slot, row_bytes) + in_row : kNoRow;
+    else return (uint32_t)max(slot, 0);  // 64-bit path: a valid row (masked keys only cost bandwidth)
+  }
+  template <int CPT>
+  __device__ __forceinline__ void load(DecStage<CPT>& st, uint32_t o, uint32_t in_row) const {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      if constexpr (OFF32) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)(o + 16 * i), 0, 0);
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vr, (int)(o + 16 * i), 0, 0);
+        st.k[i] = make_uint4(x.x, x.y, x.z, x.w);
+        st.v[i] = make_uint4(y.x, y.y, y.z, y.w);
+      } else {
+        const int64_t off = (int64_t)o * row_bytes + in_row + 16 * i;
+        st.k[i] = *reinterpret_cast<const uint4*>(kb + off);
+        st.v[i] = *reinterpret_cast<const uint4*>(vb + off);
+      }
+    }
+  }
+};
+
+template <int D, int CPT>
+__device__ __forceinline__ void dec_store(DecTile<D>& t, const DecStage<CPT>& st, int kk, int cq) {
+  __bf16* kp = t.k + kk * DecTile<D>::KS + 8 * CPT * cq;
+  __bf16* vp = t.v + kk * DecTile<D>::VS + 8 * CPT * cq;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    *reinterpret_cast<uint4*>(kp + 8 * i) = st.k[i];
+    *reinterpret_cast<uint4*>(vp + 8 * i) = st.v[i];
+  }
+}
+
+// One 64-key block for one wave's 16 rows (lane: row rr = lane % 16, lane
+// group g = lane / 16).  rel: block-local keys < rel are visible to the row.
+template <int D>
+__device__ __forceinline__ void dec_block(const DecTile<D>& t, const bf16x8 (&qf)[D / 32], f32x4 (&acc)[D / 16],
+                                          float& m_run, float& l_run, int rel, float c2, int rr, int g) {
+  constexpr int KS = DecTile<D>::KS, VS = DecTile<D>::VS;
+  constexpr int DB = D / 32, DT = D / 16;
+  f32x4 s[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t.k[(16 * kt + rr) * KS + 32 * db + 8 * g]);
+      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[db], s[kt], 0, 0, 0);
+    }
+  if (__ballot(rel < 64)) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[kt][r] = 16 * kt + 4 * g + r < rel ? s[kt][r] : -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+  mx = half_swap_max(row16_swap_max(mx));
+  // lazy rescale (see wave_block)
+  const float t_max = mx * c2;
+  const float m_new = t_max > m_run + 8.f ? t_max : m_run;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2_fast(m_run - m_use);
+  float lsp[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[kt][r] = exp2_fast(fmaf(s[kt][r], c2, -m_use));
+    lsp[kt] = (s[kt][0] + s[kt][1]) + (s[kt][2] + s[kt][3]);
+  }
+  // per-lane partial sum over this lane's keys (lanes of a row share m)
+  l_run = l_run * alpha + ((lsp[0] + lsp[1]) + (lsp[2] + lsp[3]));
+  m_run = m_new;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+  }
+  bf16x8 pk[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pk[h][r] = (__bf16)s[2 * h][r];
+      pk[h][4 + r] = (__bf16)s[2 * h + 1][r];
+    }
+  // O^T += V^T P^T: lane (rr, g) reads 8 bytes of V row 32h + 4g + rr/4 (and
+  // +16) at column 16 dt + 4 (rr % 4); the transposing read hands it the
+  // column rr of that 16 x 4 patch
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const __bf16* p0 = &t.v[(32 * h + 4 * g + (rr >> 2)) * VS + 16 * dt + 4 * (rr & 3)];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * VS));
+      // whole-word repack (element-wise extraction from the transposing
+      // read's result is not lowered correctly by this compiler)
+      const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lw.x, lw.y, hw.x, hw.y});
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[h], acc[dt], 0, 0, 0);
+    }
+}
+
+template <int D, bool OFF32>
+__global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
+  __shared__ DecTile<D> buf[2];
+  constexpr int DB = D / 32, DT = D / 16;
+  constexpr int CPT = D / 32;  // 16-byte chunks per thread: 4 threads per key row
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rr = lane & 15, g = lane >> 4;
+  const int32_t* item = a.items + (int64_t)(blockIdx.x / (unsigned)a.hkv) * kItemWords;
+  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
+  const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
+  const int jb = item[1], je = item[2];
+  const int tok_begin = tile[0], n_tok = tile[1];
+  const int group = a.group;
+  const int n_rows = n_tok * group;
+  const int row = 16 * wave + rr;
+  const int tloc = row / group;
+  int act_lo = 0, act_hi = n_tok;
+  if (tile[4] >= 0) {
+    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
+    act_lo = cr0[0];
+    act_hi = cr0[1];
+  }
+  const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
+  const bool wave_live = __ballot(row_ok) != 0;
+
+  // Q (B operand of S^T): Q[row][32 db + 8 g .. +8)
+  bf16x8 qf[DB];
+  int qpos = 0;
+  if (row_ok) {
+    const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
+    qpos = tk[1];
+    const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
+                        ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * g;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(src + 32 * db);
+  } else {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) qf[db] = bf16x8{};
+  }
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  int nblk = 0;
+  for (int j = jb; j < je; ++j) {
+    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
+    nblk += (job[2] - job[1] + 63) >> 6;
+  }
+
+  DecPool<D, OFF32> pool;
+  pool.init(a);
+  const int kk = tid >> 2, cq = tid & 3;  // staging: key row kk, chunks CPT*cq ..
+  const uint32_t in_row = (uint32_t)(kvh * D + 8 * CPT * cq) * 2;
+  // slot of this thread's key in the block the iterator is at (-1: none)
+  auto slot_of = [&](const BlockIter& it) { return it.kb + kk < it.k1 ? it.prow[it.kb + kk] : -1; };
+
+  if (nblk > 0) {
+    BlockIter it_s, it_c;
+    iter_job(a, it_s, jb);
+    it_c = it_s;
+    DecStage<CPT> r0, r1;
+    const uint32_t o0 = pool.offset(slot_of(it_s), in_row);
+    iter_next(a, it_s, je);
+    const uint32_t o1 = pool.offset(nblk > 1 ? slot_of(it_s) : -1, in_row);
+    iter_next(a, it_s, je);
+    int slot_next = nblk > 2 ? slot_of(it_s) : -1;  // block 2
+    iter_next(a, it_s, je);
+    pool.load(r0, o0, in_row);
+    pool.load(r1, o1, in_row);
+    dec_store<D, CPT>(buf[0], r0, kk, cq);
+    __syncthreads();
+
+    int cur_job = -1, lim = 0;
+    bool wave_job = false;
+    // block b: compute from buf[b & 1]; the registers of block b+1 are
+    // stored behind it; block b+2 is issued into the registers block b used
+    // Issue order matters (loads retire in order for the wait counter): the
+    // page-table read for block b+3 goes out before the K/V loads of block
+    // b+2, so the next step can wait for it without draining those loads.
+    auto step = [&](int b, DecStage<CPT>& mine, DecStage<CPT>& next) {
+      const int s2 = b + 2 < nblk ? slot_next : -1;
+      slot_next = b + 3 < nblk ? slot_of(it_s) : -1;
+      iter_next(a, it_s, je);
+      pool.load(mine, pool.offset(s2, in_row), in_row);
+      if (it_c.j != cur_job) {
+        cur_job = it_c.j;
+        const int32_t* job = a.jobs + (int64_t)cur_job * kJobWords;
+        const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+        lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+        wave_job = wave_live && __ballot(lim > job[1]) != 0;
+      }
+      if (wave_job && b < nblk) dec_block<D>(buf[b & 1], qf, acc, m_run, l_run, lim - it_c.kb, c2, rr, g);
+      dec_store<D, CPT>(buf[(b + 1) & 1], next, kk, cq);
+      iter_next(a, it_c, je);
+      __syncthreads();
+    };
+    // both half-steps unconditionally (a step past the last block only moves
+    // zeros), so every loop trip leaves the same loads outstanding
+    for (int b = 0; b < nblk; b += 2) {
+      step(b, r0, r1);
+      step(b + 1, r1, r0);
+    }
+  }
+
+  // ---- result: rows of this lane (4 lane groups share a row) ----
+  const float l_tot = half_swap_sum(row16_swap_sum(l_run));
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (tile[4] < 0) {
+    if (row_ok) {
+      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
+      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[dt][r] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * g) = v;
+      }
+    }
+    return;
+  }
+  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
+  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+    float* dst = a.ws_o + w * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) =
+          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+    if (g == 0) {
+      a.ws_ml[w * 2] = m_run;
+      a.ws_ml[w * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Wide bf16 extend kernel (head_dim 128): 8 waves, 256-row tiles.  Each K/V
 // block feeds twice the rows of the 4-wave kernel (half the loads, LDS stores
 // and barriers per flop), and each thread stages only one unit (waves 0-3 K,
@@ -794,23 +1105,34 @@ __global__ void page_table_write_kernel(int32_t* __restrict__ pt, int64_t ld, co
   for (int i = threadIdx.x; i < r[2]; i += blockDim.x) dst[i] = src[i];
 }
 
-// Page-table writes and KV scatter of one decode step in one launch:
-// workgroups [0, n_runs) each copy one page-table run, the others scatter
-// the new K/V rows (grid-stride over 16-byte vectors).
-__global__ void step_store_kernel(int32_t* __restrict__ pt, int64_t ld, const int32_t* __restrict__ runs,
-                                  const int32_t* __restrict__ run_slots, int32_t n_runs, uint4* __restrict__ kp,
-                                  uint4* __restrict__ vp, const uint4* __restrict__ kn, const uint4* __restrict__ vn,
+// Everything one decode step must write before its attention launch, in one
+// kernel: workgroups [0, n_copy) copy the work list from the mapped host
+// staging buffer to the device plan buffer (16 bytes per thread), the next
+// n_runs each write one page-table run, the rest scatter the new K/V rows.
+// Runs, run slots and new slots are read from the staging buffer too, since
+// the device copy is being written by this same launch.
+__global__ void step_store_kernel(const int4* __restrict__ stage, int4* __restrict__ dev_plan, int64_t n_vec4,
+                                  int32_t n_copy, int32_t* __restrict__ pt, int64_t ld,
+                                  const int32_t* __restrict__ runs, const int32_t* __restrict__ run_slots,
+                                  int32_t n_runs, uint4* __restrict__ kp, uint4* __restrict__ vp,
+                                  const uint4* __restrict__ kn, const uint4* __restrict__ vn,
                                   const int32_t* __restrict__ slots, int64_t n, int64_t row_vecs) {
-  if ((int32_t)blockIdx.x < n_runs) {
-    const int32_t* r = runs + (int64_t)blockIdx.x * kRunWords;
+  const int32_t bx = (int32_t)blockIdx.x;
+  if (bx < n_copy) {
+    for (int64_t i = (int64_t)bx * blockDim.x + threadIdx.x; i < n_vec4; i += (int64_t)n_copy * blockDim.x)
+      dev_plan[i] = stage[i];
+    return;
+  }
+  if (bx < n_copy + n_runs) {
+    const int32_t* r = runs + (int64_t)(bx - n_copy) * kRunWords;
     int32_t* dst = pt + (int64_t)r[0] * ld + r[1];
     const int32_t* src = run_slots + r[3];
     for (int i = threadIdx.x; i < r[2]; i += blockDim.x) dst[i] = src[i];
     return;
   }
   const int64_t total = n * row_vecs;
-  const int64_t nb = (int64_t)gridDim.x - n_runs;
-  for (int64_t i = ((int64_t)blockIdx.x - n_runs) * blockDim.x + threadIdx.x; i < total; i += nb * blockDim.x) {
+  const int64_t nb = (int64_t)gridDim.x - n_copy - n_runs;
+  for (int64_t i = ((int64_t)bx - n_copy - n_runs) * blockDim.x + threadIdx.x; i < total; i += nb * blockDim.x) {
     const int64_t tok = i / row_vecs, e = i % row_vecs;
     const int64_t dst = (int64_t)slots[tok] * row_vecs + e;
     kp[dst] = kn[i];

@@ -126,7 +126,14 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   // pools under 2 GiB are addressed with 32-bit buffer offsets (the buffer
   // resource's record count is a signed 32-bit value here)
   const bool off32 = a.pool_bytes < ((int64_t)1 << 31);
-  if (desc->dtype == RDX_BF16 && p->tile_rows == 256) {
+  if (desc->dtype == RDX_BF16 && p->tile_rows == kDecodeTileRows) {
+    if (desc->head_dim == 128)
+      e = off32 ? launch(attn_decode_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a)
+                : launch(attn_decode_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a);
+    else
+      e = off32 ? launch(attn_decode_kernel<64, true>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a)
+                : launch(attn_decode_kernel<64, false>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a);
+  } else if (desc->dtype == RDX_BF16 && p->tile_rows == 256) {
     e = off32 ? launch(attn_bf16_wide_kernel<true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a,
                        kWideThreads)
               : launch(attn_bf16_wide_kernel<false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a,
@@ -146,10 +153,24 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   return ok();
 }
 
+// Marks the current staging buffer in use until the work queued so far on
+// `st` (the copy or kernel that reads it) has completed.
+int stage_done(Plan* p, hipStream_t st) {
+  Plan::Stage& sg = p->stages[p->uploads % Plan::kStages];
+  hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(sg.event), st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  sg.pending = true;
+  p->uploads++;
+  return ok();
+}
+
 // Plan upload: checks, staging through the plan's pinned ring, the H2D copy
 // and (write_pt) the page-table write kernel.
+// zero_copy: stage only (no copy, no page-table kernel, no event): the
+// caller launches a kernel that reads the staging buffer through
+// *out_stage_dev and then calls stage_done() behind it.
 int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_table, int64_t page_table_rows,
-                hipStream_t st, bool write_pt) {
+                hipStream_t st, bool write_pt, bool zero_copy = false, const int32_t** out_stage_dev = nullptr) {
   if (!p->built) return fail(RDX_ESTATE, "rdx_plan_upload: plan not built");
   const int64_t bytes = p->total_words * 4;
   if (dev_plan_bytes < bytes) return fail(RDX_EINVAL, "rdx_plan_upload: device buffer of %lld bytes needed", (long long)bytes);
@@ -177,6 +198,8 @@ int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_t
     e = hipHostMalloc(&sg.pinned, want, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
     sg.bytes = want;
+    e = hipHostGetDevicePointer(&sg.pinned_dev, sg.pinned, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipHostGetDevicePointer");
   }
   int32_t* h = reinterpret_cast<int32_t*>(sg.pinned);
   auto put = [&](int64_t off, const std::vector<int32_t>& v) {
@@ -193,6 +216,10 @@ int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_t
   put(p->off_cptr, p->cptr);
   put(p->off_clist, p->clist);
   put(p->off_mblocks, p->mblocks);
+  if (zero_copy) {
+    *out_stage_dev = reinterpret_cast<const int32_t*>(sg.pinned_dev);
+    return ok();
+  }
   e = hipMemcpyAsync(dev_plan, sg.pinned, bytes, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
   if (write_pt && n_runs > 0) {
@@ -202,11 +229,7 @@ int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_t
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "page-table write launch");
   }
-  e = hipEventRecord(reinterpret_cast<hipEvent_t>(sg.event), st);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  sg.pending = true;
-  p->uploads++;
-  return ok();
+  return stage_done(p, st);
 }
 
 }  // namespace
@@ -322,20 +345,26 @@ int rdx_decode_step(rdx_tree* tree, rdx_plan* hplan, const rdx_attn_desc* desc, 
   if (row_bytes % 16) return undo(fail(RDX_EUNSUPPORTED, "rdx_decode_step: KV row of %lld bytes", (long long)row_bytes));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (num_reqs > 0) {
-    rc = upload_plan(p, io->dev_plan, io->dev_plan_bytes, io->page_table, io->page_table_rows, st, false);
+    const int32_t* hs = nullptr;  // the staged work list, device-addressable
+    rc = upload_plan(p, io->dev_plan, io->dev_plan_bytes, io->page_table, io->page_table_rows, st, false, true, &hs);
     if (rc) return undo(rc);
-    const int32_t* db = reinterpret_cast<const int32_t*>(io->dev_plan);
     const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
     const int64_t row_vecs = row_bytes / 16, total = (int64_t)num_reqs * row_vecs;
+    const int64_t n_vec4 = (p->total_words + 3) / 4;  // total_words is a multiple of 16
+    int64_t n_copy = (n_vec4 + 255) / 256;
+    if (n_copy > 64) n_copy = 64;
     int64_t kv_blocks = (total + 255) / 256;
     if (kv_blocks > 65536) kv_blocks = 65536;
-    hipLaunchKernelGGL(step_store_kernel, dim3((unsigned)(n_runs + kv_blocks)), dim3(256), 0, st, io->page_table, ld,
-                       db + p->off_runs, db + p->off_run_slots, (int32_t)n_runs,
+    hipLaunchKernelGGL(step_store_kernel, dim3((unsigned)(n_copy + n_runs + kv_blocks)), dim3(256), 0, st,
+                       reinterpret_cast<const int4*>(hs), reinterpret_cast<int4*>(io->dev_plan), n_vec4,
+                       (int32_t)n_copy, io->page_table, ld, hs + p->off_runs, hs + p->off_run_slots, (int32_t)n_runs,
                        reinterpret_cast<uint4*>(io->k_pool), reinterpret_cast<uint4*>(io->v_pool),
                        reinterpret_cast<const uint4*>(io->k_new), reinterpret_cast<const uint4*>(io->v_new),
-                       db + p->off_new, (int64_t)num_reqs, row_vecs);
+                       hs + p->off_new, (int64_t)num_reqs, row_vecs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return undo(hip_fail(e, "step store launch"));
+    rc = stage_done(p, st);
+    if (rc) return undo(rc);
     rc = launch_attention(desc, hplan, RDX_PLAN_DECODE, io->dev_plan, io->q, io->k_pool, io->v_pool, io->page_table,
                           io->o, io->workspace, io->workspace_bytes, stream);
     if (rc) return undo(rc);

@@ -18,6 +18,7 @@ namespace rdx {
 
 constexpr int kTileRows = 128;   // query rows (token x grouped head) per tile
 constexpr int kKeyBlock = 64;    // keys per inner iteration of the kernels
+constexpr int kDecodeTileRows = 64;  // query rows per tile of the bf16 decode kernel
 
 // Record layouts (int32 words) -- shared with the device code.
 constexpr int kItemWords = 4;     // tile, job_begin, job_end, contrib (one per key chunk; run for every KV head)
@@ -52,6 +53,7 @@ struct Plan {
   static constexpr int kStages = 4;
   struct Stage {
     void* pinned = nullptr;
+    void* pinned_dev = nullptr;  // the same memory as the device addresses it
     int64_t bytes = 0;
     void* event = nullptr;
     bool pending = false;
@@ -59,7 +61,7 @@ struct Plan {
   int64_t uploads = 0;
 
   // query rows per tile: 256 for the wide bf16 head_dim-128 extend kernel,
-  // kTileRows otherwise
+  // kDecodeTileRows for the bf16 decode kernel, kTileRows otherwise
   int tile_rows = kTileRows;
   int group() const { return desc.num_q_heads / desc.num_kv_heads; }
   int tile_tokens() const { return tile_rows / group(); }
