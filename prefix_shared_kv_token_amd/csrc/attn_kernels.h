@@ -205,6 +205,26 @@ struct PoolReader {
     r.d = chunk(s.w, off);
     return r;
   }
+  // valid == false: no row is wanted.  With 32-bit offsets the loads get an
+  // offset past the buffer's end and return zeros without a memory access;
+  // otherwise they read the (valid) rows anyway.
+  __device__ __forceinline__ Rows4 rows_if(const int4& s, uint32_t off, bool valid) const {
+    if constexpr (OFF32) {
+      auto o = [&](int slot) { return valid ? __umul24((uint32_t)slot, row_bytes) + off : 0x80000000u; };
+      auto ld = [&](uint32_t x) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)x, 0, 0);
+        return make_uint4(v.x, v.y, v.z, v.w);
+      };
+      Rows4 r;
+      r.a = ld(o(s.x));
+      r.b = ld(o(s.y));
+      r.c = ld(o(s.z));
+      r.d = ld(o(s.w));
+      return r;
+    } else {
+      return rows(s, off);
+    }
+  }
 };
 
 template <int D>
@@ -288,18 +308,16 @@ __device__ __forceinline__ void sched_lds_mfma() {
   __builtin_amdgcn_sched_group_barrier(kMfma, 4, 0);
 }
 
-// One 64-key block for one wave's 32 query rows: S^T = K Q^T on MFMA, mask
-// (keys with block-local index >= rel are invisible to this lane's row),
-// online softmax in base 2 with lazy rescale, O^T += V^T P^T on MFMA.
+// S^T = K Q^T for the 64 keys of tile t x this wave's 32 queries.  The two
+// 32-key halves are interleaved (independent accumulators) and the
+// scheduler is told to keep LDS operand reads several MFMAs ahead.
 template <int D>
-__device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qreg)[D / 16], f32x16 (&acc)[D / 32],
-                                           float& m_run, float& l_run, int rel, float c2, int li, int hi) {
-  constexpr int KS = KVTile<D>::KS, VS = KVTile<D>::VS;
-  constexpr int KSTEPS = D / 16, DB = D / 32;
-  // S^T = K Q^T for 64 keys x this wave's 32 queries.  The two 32-key
-  // halves are interleaved (independent accumulators) and the scheduler is
-  // told to keep LDS operand reads several MFMAs ahead.
-  f32x16 s[2] = {f32x16{}, f32x16{}};
+__device__ __forceinline__ void wave_scores(const KVTile<D>& t, const bf16x8 (&qreg)[D / 16], f32x16 (&s)[2], int li,
+                                            int hi) {
+  constexpr int KS = KVTile<D>::KS;
+  constexpr int KSTEPS = D / 16;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
@@ -308,6 +326,16 @@ __device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qr
       s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb2], 0, 0, 0);
     }
   sched_lds_mfma<2 * KSTEPS>();
+}
+
+// The rest of a block once its scores s are in: mask (block-local keys >=
+// rel are invisible to this lane's row), online softmax in base 2 with lazy
+// rescale, O^T += V^T P^T from tile t.
+template <int D>
+__device__ __forceinline__ void wave_update(const KVTile<D>& t, f32x16 (&s)[2], f32x16 (&acc)[D / 32], float& m_run,
+                                            float& l_run, int rel, float c2, int li, int hi) {
+  constexpr int VS = KVTile<D>::VS;
+  constexpr int DB = D / 32;
   // mask (only where some lane of the wave needs it) + online softmax, base 2
     if (__ballot(rel < 64)) {
 #pragma unroll
@@ -367,7 +395,15 @@ __device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qr
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], acc[db], 0, 0, 0);
     }
   sched_lds_mfma<4 * DB>();
+}
 
+// One 64-key block for one wave's 32 query rows: scores, then update.
+template <int D>
+__device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qreg)[D / 16], f32x16 (&acc)[D / 32],
+                                           float& m_run, float& l_run, int rel, float c2, int li, int hi) {
+  f32x16 s[2];
+  wave_scores<D>(t, qreg, s, li, hi);
+  wave_update<D>(t, s, acc, m_run, l_run, rel, c2, li, hi);
 }
 
 // Final result of one lane's row: the normalised output (direct tiles) or
@@ -887,20 +923,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
 // Wide bf16 extend kernel (head_dim 128): 8 waves, 256-row tiles.  Each K/V
 // block feeds twice the rows of the 4-wave kernel (half the loads, LDS stores
 // and barriers per flop), and each thread stages only one unit (waves 0-3 K,
-// waves 4-7 V), which leaves registers for two blocks of prefetch: at block
-// b the K/V rows of block b+2 are being loaded, block b+1 waits in registers,
-// and the page-table slots of block b+3 are read.
+// waves 4-7 V).
+//
+// Ping-pong between the two waves of each SIMD (waves w and w+4): waves 0-3
+// run block b as scores -> softmax -> P.V, waves 4-7 run softmax(b) -> P.V(b)
+// -> scores(b+1), so one wave's MFMA runs line up with the other's softmax
+// instead of both waves contending for the matrix core and then both idling
+// it.  This needs block b+1 in LDS while block b is computed: three LDS
+// buffers (block b, b+1, and b+2 being staged); K/V of block b+2 wait in
+// registers while block b+3 is being loaded, and the page-table slots of block
+// b+4 are read.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 512;
+
+// Per-wave view of the job a key block belongs to.
+struct JobView {
+  int job = -1, lim = 0;
+  bool live = false;  // some row of this wave attends to the job
+};
+
+__device__ __forceinline__ void job_view(const AttnArgs& a, const BlockIter& it, JobView& v, bool row_ok, int tloc,
+                                         int qpos, bool wave_live) {
+  if (it.j == v.job) return;
+  v.job = it.j;
+  const int32_t* job = a.jobs + (int64_t)it.j * kJobWords;
+  const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+  v.lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+  v.live = wave_live && __ballot(v.lim > job[1]) != 0;
+}
 
 template <bool OFF32>
 __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArgs a) {
   constexpr int D = 128, KSTEPS = D / 16, DB = D / 32, CH = D / 8;
-  __shared__ KVTile<D> buf[2];
+  __shared__ KVTile<D> buf[3];
   __shared__ int slot_ring[2][64];
 
   const int tid = threadIdx.x;
-  const bool doK = tid < 256;
+  // waves 0-3 stage K, 4-7 V; taken from lane 0 so the compiler sees a
+  // wave-uniform choice (the pool's buffer resource stays in scalar registers)
+  const bool doK = __builtin_amdgcn_readfirstlane(tid) < 256;
   const int u = tid & 255;
   const int qd = doK ? u / CH : u % 16;  // K units: chunk fastest; V units: key quad fastest
   const int cc = doK ? u % CH : u / 16;
@@ -915,6 +976,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   const int group = a.group;
   const int n_rows = n_tok * group;
   const int lane = tid & 63, wave = tid >> 6;
+  const bool ahead = wave >= 4;  // waves that compute scores one block ahead
   const int li = lane & 31, hi = lane >> 5;
   const int row = wave * 32 + li;
   const int tloc = row / group;
@@ -957,9 +1019,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
     nblk += (job[2] - job[1] + 63) >> 6;
   }
 
-  auto issue = [&](Rows4& r, const int* slots) {
+  auto issue = [&](Rows4& r, const int* slots, bool valid = true) {
     const int4 sl = *reinterpret_cast<const int4*>(slots + 4 * qd);
-    r = pool.rows(sl, off);
+    r = pool.rows_if(sl, off, valid);
   };
   auto stage = [&](KVTile<D>& t, const Rows4& r) {
     if (doK)
@@ -969,11 +1031,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   };
 
   if (nblk > 0) {
-    BlockIter it_slot, it_comp;
+    BlockIter it_slot, it_comp, it_next;
     iter_job(a, it_slot, jb);
     it_comp = it_slot;
     Rows4 rA, rB;
-    // ---- prologue: block 0 in LDS, block 1 in registers, slots of block 2 in the ring ----
+    // ---- prologue: blocks 0 and 1 in LDS, block 2 loading, slots of block 3 in the ring ----
     if (tid < 64) slot_ring[0][tid] = block_slot(it_slot, tid);
     iter_next(a, it_slot, je);
     if (nblk > 1) {
@@ -989,36 +1051,57 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
       iter_next(a, it_slot, je);
     }
     stage(buf[0], rA);
+    if (nblk > 1) stage(buf[1], rB);
+    __syncthreads();
+    if (nblk > 2) issue(rA, slot_ring[0]);
+    if (nblk > 3) {  // ring[1] was last read before the second barrier
+      if (tid < 64) slot_ring[1][tid] = block_slot(it_slot, tid);
+      iter_next(a, it_slot, je);
+    }
     __syncthreads();
 
-    int cur_job = -1, lim = 0;
-    bool wave_job = false;
-    // one key block: rcur holds nothing live (it is reloaded with block b+2),
-    // rnext holds block b+1 (staged into LDS after the compute)
+    JobView vc, vn;  // jobs of the block being finished and of the block after it
+    it_next = it_comp;
+    iter_next(a, it_next, je);
+    f32x16 s[2];
+    job_view(a, it_comp, vc, row_ok, tloc, qpos, wave_live);
+    if (ahead && vc.live) wave_scores<D>(buf[0], qreg, s, li, hi);
+
+    int bc = 0;  // LDS buffer of block b
+    // block b: rnext holds block b+2 (staged behind the compute), rcur is
+    // reloaded with block b+3 from ring[(b+1) & 1]; the slots of block b+4 go
+    // to ring[b & 1], which the previous step read.  Loads retire in order
+    // for the wait counter, so the page-table read goes out before the K/V
+    // loads, and nothing is loaded or staged under a branch (past the last
+    // block the loads are out of range and the staged tile is never used):
+    // each step then waits only for the block it stages.
     auto step = [&](int b, Rows4& rcur, Rows4& rnext) {
-      if (b + 2 < nblk) issue(rcur, slot_ring[b & 1]);
-      int slot_after = 0;
-      const bool more = b + 3 < nblk;
-      if (more) {
-        if (tid < 64) slot_after = block_slot(it_slot, tid);
-        iter_next(a, it_slot, je);
+      const bool more = b + 4 < nblk;
+      const int slot_after = block_slot(it_slot, tid & 63);  // clamped: always a valid position
+      if (more) iter_next(a, it_slot, je);
+      issue(rcur, slot_ring[(b + 1) & 1], b + 3 < nblk);
+      const int bn = bc == 2 ? 0 : bc + 1, bs = bn == 2 ? 0 : bn + 1;
+      if (b < nblk) {
+        job_view(a, it_comp, vc, row_ok, tloc, qpos, wave_live);
+        if (vc.live) {
+          if (!ahead) wave_scores<D>(buf[bc], qreg, s, li, hi);
+          wave_update<D>(buf[bc], s, acc, m_run, l_run, vc.lim - it_comp.kb, c2, li, hi);
+        }
+        if (ahead && b + 1 < nblk) {
+          job_view(a, it_next, vn, row_ok, tloc, qpos, wave_live);
+          if (vn.live) wave_scores<D>(buf[bn], qreg, s, li, hi);
+        }
       }
-      if (it_comp.j != cur_job) {
-        cur_job = it_comp.j;
-        const int32_t* job = a.jobs + (int64_t)cur_job * kJobWords;
-        const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
-        lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
-        wave_job = wave_live && __ballot(lim > job[1]) != 0;
-      }
-      if (wave_job) wave_block<D>(buf[b & 1], qreg, acc, m_run, l_run, lim - it_comp.kb, c2, li, hi);
-      if (b + 1 < nblk) stage(buf[(b + 1) & 1], rnext);
-      if (more && tid < 64) slot_ring[(b + 1) & 1][tid] = slot_after;
+      stage(buf[bs], rnext);
+      if (more && tid < 64) slot_ring[b & 1][tid] = slot_after;
       iter_next(a, it_comp, je);
+      iter_next(a, it_next, je);
+      bc = bn;
       __syncthreads();
     };
     for (int b = 0; b < nblk; b += 2) {
-      step(b, rA, rB);
-      if (b + 1 < nblk) step(b + 1, rB, rA);
+      step(b, rB, rA);
+      step(b + 1, rA, rB);
     }
   }
   write_result<D>(a, tile, item, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
