@@ -101,6 +101,38 @@ int rdx_insert(rdx_tree* tree, const int32_t* tokens, const int32_t* slots, int6
  * is left; *out_freed = tokens freed (may exceed n_tokens). */
 int rdx_evict(rdx_tree* tree, int64_t n_tokens, int64_t* out_freed);
 
+/* Batch admission -- the serving loop's admit step for a whole batch in one
+ * call, the same call sequence as doing it request by request (SGLang
+ * explainer, RadixAttention section: match the prompt against the tree,
+ * lock the matched path, allocate slots for the rest, evicting LRU leaves
+ * when short).  Request i's prompt is tokens[offsets[i] .. offsets[i+1])
+ * (length n_i <= ld) and it owns host page-table row rows[i] (< num_rows) of
+ * host_page_table (host int32 [num_rows][ld]).  For i = 0, 1, ...:
+ * rdx_match_prefix (its slots go to row[0..m_i)), rdx_lock of the matched
+ * node, rdx_alloc(n_i - m_i) into row[m_i..n_i); out_matched[i] = m_i,
+ * out_node[i] = the node, and the new slots are also appended to
+ * out_new_slots (request-major; capacity offsets[num_reqs] - offsets[0]).
+ * *out_admitted = the number of requests admitted.  On an error (EINVAL,
+ * ENOSPC, ESTATE) at request i, requests 0..i-1 stay admitted (locked,
+ * rows written), request i holds no lock and no slots, and the later
+ * requests are untouched. */
+int rdx_admit(rdx_tree* tree, int32_t num_reqs, const int32_t* tokens, const int64_t* offsets,
+              const int32_t* rows, int32_t* host_page_table, int64_t num_rows, int64_t ld,
+              int64_t* out_matched, int64_t* out_node, int32_t* out_new_slots, int32_t* out_admitted);
+
+/* Batch completion (SGLang explainer, RadixAttention section: after a
+ * request completes, its tokens are inserted so later requests can reuse
+ * them), request by request: insert tokens[offsets[i] .. offsets[i+1])
+ * (prompt + generated, n_i <= ld) with the slots of host page-table row
+ * rows[i] positions 0..n_i-1; free the request's duplicates in
+ * [matched[i], present) where present is the length the tree already held;
+ * unlock node[i].  *out_done = the number of requests finished; on an error
+ * (EINVAL, ESTATE) at request i the earlier ones stay finished and request i
+ * is untouched. */
+int rdx_finish(rdx_tree* tree, int32_t num_reqs, const int32_t* tokens, const int64_t* offsets,
+               const int32_t* rows, const int32_t* host_page_table, int64_t num_rows, int64_t ld,
+               const int64_t* matched, const int64_t* node, int32_t* out_done);
+
 typedef struct rdx_stats {
   int64_t num_slots;
   int64_t free;      /* slots in the free set */

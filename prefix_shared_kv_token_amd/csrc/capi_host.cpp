@@ -1,7 +1,9 @@
 // C ABI: host-side entry points (tree, planner).  The device entry points
 // live in device.hip.
 #include <cmath>
+#include <cstring>
 #include <new>
+#include <string>
 
 #include "common.h"
 #include "plan.h"
@@ -69,6 +71,75 @@ int rdx_insert(rdx_tree* t, const int32_t* tokens, const int32_t* slots, int64_t
 int rdx_evict(rdx_tree* t, int64_t n_tokens, int64_t* out_freed) {
   if (!t) return fail(RDX_EINVAL, "rdx_evict: null tree");
   return t->impl.evict(n_tokens, out_freed);
+}
+
+int rdx_admit(rdx_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* offsets, const int32_t* rows,
+              int32_t* host_page_table, int64_t num_rows, int64_t ld, int64_t* out_matched, int64_t* out_node,
+              int32_t* out_new_slots, int32_t* out_admitted) {
+  if (!t || !out_admitted || num_reqs < 0 || num_rows <= 0 || ld <= 0)
+    return fail(RDX_EINVAL, "rdx_admit: bad arguments");
+  *out_admitted = 0;
+  if (num_reqs == 0) return rdx::ok();
+  if (!tokens || !offsets || !rows || !host_page_table || !out_matched || !out_node || !out_new_slots)
+    return fail(RDX_EINVAL, "rdx_admit: null array");
+  rdx::RadixTree& tr = t->impl;
+  int64_t nn = 0;  // new slots written so far
+  for (int32_t i = 0; i < num_reqs; ++i) {
+    const int64_t n = offsets[i + 1] - offsets[i];
+    const int32_t r = rows[i];
+    if (n < 0 || n > ld || r < 0 || r >= num_rows)
+      return fail(RDX_EINVAL, "rdx_admit: request %d: length %lld, row %d (ld %lld, %lld rows)", i, (long long)n, r,
+                  (long long)ld, (long long)num_rows);
+    int32_t* row = host_page_table + (int64_t)r * ld;
+    int64_t m = 0, node = 0;
+    int rc = tr.match_prefix(tokens + offsets[i], n, row, &m, &node);
+    if (rc) return rc;
+    rc = tr.lock(node);
+    if (rc) return rc;
+    rc = tr.alloc(n - m, row + m);
+    if (rc) {
+      const std::string msg = rdx::last_error();
+      tr.unlock(node);
+      rdx::last_error() = msg;
+      return rc;
+    }
+    std::memcpy(out_new_slots + nn, row + m, (size_t)(n - m) * sizeof(int32_t));
+    nn += n - m;
+    out_matched[i] = m;
+    out_node[i] = node;
+    *out_admitted = i + 1;
+  }
+  return rdx::ok();
+}
+
+int rdx_finish(rdx_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* offsets, const int32_t* rows,
+               const int32_t* host_page_table, int64_t num_rows, int64_t ld, const int64_t* matched,
+               const int64_t* node, int32_t* out_done) {
+  if (!t || !out_done || num_reqs < 0 || num_rows <= 0 || ld <= 0) return fail(RDX_EINVAL, "rdx_finish: bad arguments");
+  *out_done = 0;
+  if (num_reqs == 0) return rdx::ok();
+  if (!tokens || !offsets || !rows || !host_page_table || !matched || !node)
+    return fail(RDX_EINVAL, "rdx_finish: null array");
+  rdx::RadixTree& tr = t->impl;
+  for (int32_t i = 0; i < num_reqs; ++i) {
+    const int64_t n = offsets[i + 1] - offsets[i];
+    const int32_t r = rows[i];
+    if (n < 0 || n > ld || r < 0 || r >= num_rows || matched[i] < 0 || matched[i] > n)
+      return fail(RDX_EINVAL, "rdx_finish: request %d: length %lld, row %d, matched %lld", i, (long long)n, r,
+                  (long long)matched[i]);
+    const int32_t* row = host_page_table + (int64_t)r * ld;
+    int64_t present = 0, nd = 0;
+    int rc = tr.insert(tokens + offsets[i], row, n, &present, &nd);
+    if (rc) return rc;
+    if (present > matched[i]) {
+      rc = tr.free_slots(row + matched[i], present - matched[i]);
+      if (rc) return rc;
+    }
+    rc = tr.unlock(node[i]);
+    if (rc) return rc;
+    *out_done = i + 1;
+  }
+  return rdx::ok();
 }
 
 int rdx_tree_stats(const rdx_tree* t, rdx_stats* out) {

@@ -272,10 +272,12 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
 
   // ---- split into items ----
   const int hkv = desc.num_kv_heads;
-  // default launch size the split aims for: extend only splits when fewer
-  // than ~one round of workgroups (2 per CU) exists; decode aims for ~2 per
-  // CU (measured best: larger chunks amortise the Q load and partial write)
-  int64_t target = target_items > 0 ? target_items : 512;
+  // default launch size the split aims for (about one round of workgroups):
+  // extend splits only when fewer work items than that exist -- 256 for the
+  // 256-row kernel (one workgroup per CU), 512 for the 128-row one (two);
+  // decode aims for ~2 per CU (measured best: larger chunks amortise the Q
+  // load and the partial write, smaller ones add merge work)
+  int64_t target = target_items > 0 ? target_items : (kind == RDX_PLAN_EXTEND && tile_rows == 256 ? 256 : 512);
   int64_t chunk = INT64_MAX;
   if ((int64_t)ntiles * hkv < target && total_cost > 0) {
     int64_t per_kvh = std::max<int64_t>(1, target / hkv);

@@ -43,10 +43,28 @@ class WorkloadRun:
         self.dv = torch.empty_like(self.dk)
         if T and R:
             wl.fill_decode(self.dq, self.dk, self.dv)
-        self.prompts = [[wl.prompt_tokens(r) for r in ph.requests] for ph in wl.phases]
-        self.generated = wl.decode_token_matrix()
+        self._phase_arrays()
         self.extend_tokens = [sum(r.own_len for r in ph.requests) for ph in wl.phases]
         self.decode_tokens = T * R
+
+    def _phase_arrays(self):
+        """Per phase: the prompts concatenated, the matched lengths the
+        synthetic queries assume, and the full sequences finish() inserts."""
+        wl, cfg = self.wl, self.cfg
+        self.prompts = [[wl.prompt_tokens(r) for r in ph.requests] for ph in wl.phases]
+        self.generated = wl.decode_token_matrix()
+        self.ptok, self.poff, self.expect, self.seq = [], [], [], []
+        for pi, ph in enumerate(wl.phases):
+            ps = self.prompts[pi]
+            self.ptok.append(np.concatenate(ps).astype(np.int32))
+            self.poff.append(np.concatenate([[0], np.cumsum([len(p) for p in ps])]).astype(np.int64))
+            self.expect.append(np.array([r.prompt_len - r.own_len for r in ph.requests], np.int64))
+            if pi == len(wl.phases) - 1 and cfg.decode_steps:
+                full = [np.concatenate([p, self.generated[i]]) for i, p in enumerate(ps)]
+                self.seq.append((np.concatenate(full).astype(np.int32),
+                                 np.concatenate([[0], np.cumsum([len(f) for f in full])]).astype(np.int64)))
+            else:
+                self.seq.append((self.ptok[-1], self.poff[-1]))
 
     def fragment(self, tree):
         """Leave only a random subset of the pool free (the rest held as
@@ -59,8 +77,10 @@ class WorkloadRun:
         tree.free(keep_free)
 
     def run(self, keep_outputs: bool = True, timers: dict | None = None, record: bool = False):
-        """One pass of every phase.  record=True keeps each attention launch
-        (its own plan and buffers) in out["launches"] for Runtime.replay."""
+        """One pass of every phase.  keep_outputs=False keeps only the last
+        decode step's output and no page-table rows.  record=True keeps each
+        attention launch (its own plan and buffers) in out["launches"] for
+        Runtime.replay."""
         torch = self.torch
         rt = self.rt
         rt.reset()
@@ -71,12 +91,11 @@ class WorkloadRun:
         n_phases = len(self.wl.phases)
         dec_buf = None
         for pi, ph in enumerate(self.wl.phases):
-            reqs = rt.admit(self.prompts[pi])
-            for r, wr in zip(reqs, ph.requests):
-                if r.matched != wr.prompt_len - wr.own_len:
-                    raise RuntimeError(f"request {wr.rid}: matched {r.matched}, expected "
-                                       f"{wr.prompt_len - wr.own_len} (the synthetic queries cover only the "
-                                       f"uncached part)")
+            reqs = rt.admit_tokens(self.ptok[pi], self.poff[pi])
+            if not np.array_equal(reqs.matched, self.expect[pi]):
+                j = int(np.flatnonzero(reqs.matched != self.expect[pi])[0])
+                raise RuntimeError(f"request {ph.requests[j].rid}: matched {int(reqs.matched[j])}, expected "
+                                   f"{int(self.expect[pi][j])} (the synthetic queries cover only the uncached part)")
             q, k, v = self.inputs[pi]
             tm = self._timer(timers, "extend")
             o = rt.extend(reqs, q, k, v, timer=tm)
@@ -94,9 +113,10 @@ class WorkloadRun:
                     rt.decode_step(reqs, self.dq[t], self.dk[t], self.dv[t],
                                    o=dec_buf[t if keep_outputs else 0], timer=tm)
                 out["decode"] = dec_buf
-            out["matched"].append([r.matched for r in reqs])
-            out["rows"].append([rt.host_pt[r.row, : r.kv_len].copy() for r in reqs])
-            rt.finish(reqs, self.generated if leaf and cfg.decode_steps else None)
+            out["matched"].append(reqs.matched.tolist())
+            if keep_outputs:
+                out["rows"].append([rt.host_pt[r, :k].copy() for r, k in zip(reqs.rows, reqs.kv_len)])
+            rt.finish(reqs, seq=self.seq[pi])
         out["launches"] = rt.record
         rt.record = None
         return out

@@ -77,6 +77,8 @@ _SIGS = {
     "rdx_free": (ctypes.c_int, [vp, i32p, i64]),
     "rdx_insert": (ctypes.c_int, [vp, i32p, i32p, i64, i64p, i64p]),
     "rdx_evict": (ctypes.c_int, [vp, i64, i64p]),
+    "rdx_admit": (ctypes.c_int, [vp, i32, i32p, i64p, i32p, i32p, i64, i64, i64p, i64p, i32p, i32p]),
+    "rdx_finish": (ctypes.c_int, [vp, i32, i32p, i64p, i32p, i32p, i64, i64, i64p, i64p, i32p]),
     "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
     "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
     "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),

@@ -9,13 +9,14 @@ batch here.  All computation runs in the library; this module marshals
 arguments and keeps a host copy of the page-table rows for `finish`.
 
 Protocol (the oracle models the same call sequence):
-  admit:   per request in order: match_prefix, lock, alloc(n - m)
+  admit:   one rdx_admit: per request in order match_prefix, lock,
+           alloc(n - m), page-table row on the host
   extend:  one plan upload (page-table rows + work list), kv_store of the new
            tokens, one extend-attention launch
-  decode:  per step one alloc(R) (slots to requests in order), one plan
-           upload, kv_store of the R new tokens, one decode-attention launch
-  finish:  per request: insert(prompt + generated, row), free duplicates,
-           unlock
+  decode:  per step one rdx_decode_step: alloc(R) (slots to requests in
+           order), plan, upload, KV scatter, decode attention
+  finish:  one rdx_finish: per request insert(prompt + generated, row), free
+           duplicates, unlock
 """
 from __future__ import annotations
 
@@ -35,59 +36,74 @@ class _RowState:
         self.written = np.zeros(rows, np.int32)
 
 
+class Batch:
+    """A batch admitted by a Runtime: per-request arrays in batch order (the
+    concatenated prompts, their page-table rows, matched lengths, locked
+    nodes, and the newly allocated slots, request-major).  While the batch
+    holds its rows, the requests' KV lengths and written-entry counts live
+    in the runtime's per-row arrays (a decode step updates them in one
+    call); finish() freezes them into the batch.  Indexing gives a Request
+    view of one request."""
+
+    def __init__(self, rs: _RowState, tokens, offsets, rows, matched, nodes, new_slots):
+        self._rs = rs
+        self.n = len(rows)
+        self.tokens, self.offsets = tokens, offsets
+        self.rows = rows                      # int32
+        self.rows64 = rows.astype(np.int64)
+        self.matched, self.nodes = matched, nodes  # int64
+        self.lens = np.diff(offsets)
+        self.q_lens = self.lens - matched
+        self.new_off = np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int64)
+        self.new_slots = new_slots            # int32, request-major
+        self._final = None
+        # fixed arguments of the per-token decode call
+        self.slots = np.empty(max(1, self.n), np.int32)
+        self.slots_p = rdx._p32(self.slots)
+        self.node_p = self.nodes.ctypes.data_as(rdx.i64p)
+        self.row_p = rdx._p32(self.rows)
+
+    def __len__(self):
+        return self.n
+
+    def __getitem__(self, i):
+        if not -self.n <= i < self.n:
+            raise IndexError(i)
+        return Request(self, i % self.n)
+
+    def __iter__(self):
+        return (Request(self, i) for i in range(self.n))
+
+    @property
+    def kv_len(self) -> np.ndarray:
+        return self._final[0] if self._final is not None else self._rs.kv_len[self.rows64]
+
+    @property
+    def written(self) -> np.ndarray:
+        return self._final[1] if self._final is not None else self._rs.written[self.rows64]
+
+
 class Request:
-    """A request admitted by a Runtime.  While it holds its page-table row,
-    its KV length and written-entry count live in the runtime's per-row
-    arrays (a decode step updates a whole batch at once); finish() freezes
-    them into the request."""
+    """View of request i of a Batch."""
 
-    __slots__ = ("prompt", "matched", "node", "row", "new_slots", "_rs", "_frozen")
+    __slots__ = ("_b", "_i")
 
-    def __init__(self, prompt, matched, node, row, new_slots, rs: _RowState, kv_len: int, written: int = 0):
-        self.prompt, self.matched, self.node, self.row, self.new_slots = prompt, matched, node, row, new_slots
-        self._rs, self._frozen = rs, None
-        rs.kv_len[row] = kv_len
-        rs.written[row] = written
+    def __init__(self, batch: Batch, i: int):
+        self._b, self._i = batch, i
+
+    prompt = property(lambda self: self._b.tokens[self._b.offsets[self._i]:self._b.offsets[self._i + 1]])
+    matched = property(lambda self: int(self._b.matched[self._i]))
+    node = property(lambda self: int(self._b.nodes[self._i]))
+    row = property(lambda self: int(self._b.rows[self._i]))
+    new_slots = property(lambda self: self._b.new_slots[self._b.new_off[self._i]:self._b.new_off[self._i + 1]])
 
     @property
     def kv_len(self) -> int:
-        return self._frozen[0] if self._frozen else int(self._rs.kv_len[self.row])
-
-    @kv_len.setter
-    def kv_len(self, v: int):
-        self._rs.kv_len[self.row] = v
+        return int(self._b.kv_len[self._i])
 
     @property
     def written(self) -> int:
-        return self._frozen[1] if self._frozen else int(self._rs.written[self.row])
-
-    @written.setter
-    def written(self, v: int):
-        self._rs.written[self.row] = v
-
-    def _freeze(self):
-        self._frozen = (self.kv_len, self.written)
-
-
-class _DecodeBatch:
-    """Node and row arrays of one decode batch, in batch order, and the slot
-    buffer its steps allocate into (built once per batch)."""
-
-    def __init__(self, reqs):
-        n = len(reqs)
-        self.reqs, self.n = reqs, n
-        self.node = np.fromiter((r.node for r in reqs), np.int64, n)
-        self.row = np.fromiter((r.row for r in reqs), np.int32, n)
-        self.row64 = self.row.astype(np.int64)
-        self.slots = np.empty(max(1, n), np.int32)
-        p32 = rdx._p32
-        self.slots_p = p32(self.slots)
-        self.node_p = self.node.ctypes.data_as(rdx.i64p)
-        self.row_p = p32(self.row)
-
-    def matches(self, reqs) -> bool:
-        return (reqs is self.reqs and len(reqs) == self.n
-                and (self.n == 0 or (reqs[0].row == self.row[0] and reqs[-1].row == self.row[-1])))
+        return int(self._b.written[self._i])
 
 
 class Runtime:
@@ -118,7 +134,6 @@ class Runtime:
         self.workspace = torch.zeros(0, dtype=torch.uint8, device=self.device)
         self.last_info = {}
         self.record = None   # a list to keep every launch (plan, buffers) for replay
-        self._dec = None     # arrays of the current decode batch
         self._info = rdx.PlanInfo()
         self._info_ref = ctypes.byref(self._info)
         self._desc_ref = ctypes.byref(self.desc)
@@ -135,7 +150,6 @@ class Runtime:
         """Empty tree and page-table rows; pools and buffers are kept."""
         self.tree = rdx.Tree(self.num_slots)
         self.free_rows = list(range(self.max_rows - 1, -1, -1))
-        self._dec = None
 
     # ------------------------------------------------------------ buffers
     def _dev_plan(self, kind: int, nbytes: int):
@@ -152,20 +166,47 @@ class Runtime:
         return self.workspace
 
     # ------------------------------------------------------------ protocol
-    def admit(self, prompts) -> list:
-        reqs = []
-        for p in prompts:
-            p = np.ascontiguousarray(p, np.int32)
-            m, slots, node = self.tree.match_prefix(p)
-            self.tree.lock(node)
-            new = self.tree.alloc(len(p) - m).copy()
-            if not self.free_rows:
-                raise RuntimeError("no free page-table row")
-            row = self.free_rows.pop()
-            self.host_pt[row, :m] = slots
-            self.host_pt[row, m:len(p)] = new
-            reqs.append(Request(p, m, node, row, new, self._rs, len(p), 0))
-        return reqs
+    def admit(self, prompts) -> Batch:
+        """Admit a list of prompts (token id arrays) as one batch."""
+        prompts = [np.asarray(p, np.int32) for p in prompts]
+        offsets = np.concatenate([[0], np.cumsum([len(p) for p in prompts])]).astype(np.int64)
+        tokens = np.concatenate(prompts) if prompts else np.zeros(0, np.int32)
+        return self.admit_tokens(tokens, offsets)
+
+    def admit_tokens(self, tokens: np.ndarray, offsets: np.ndarray) -> Batch:
+        """Admit the prompts tokens[offsets[i]:offsets[i+1]] in one rdx_admit
+        call: per request, match, lock the matched node, allocate the rest,
+        and fill its page-table row on the host."""
+        tokens = np.ascontiguousarray(tokens, np.int32)
+        offsets = np.ascontiguousarray(offsets, np.int64)
+        n = len(offsets) - 1
+        if n > len(self.free_rows):
+            raise RuntimeError(f"no free page-table rows for {n} requests ({len(self.free_rows)} free)")
+        cut = len(self.free_rows) - n
+        rows = np.array(self.free_rows[cut:][::-1], np.int32)
+        del self.free_rows[cut:]
+        matched = np.zeros(n, np.int64)
+        nodes = np.zeros(n, np.int64)
+        new_slots = np.empty(max(1, int(offsets[-1] - offsets[0])), np.int32)
+        done = rdx.i32()
+        p32, p64 = rdx._p32, (lambda x: x.ctypes.data_as(rdx.i64p))
+        rc = rdx.lib().rdx_admit(self.tree.handle, n, p32(tokens), p64(offsets), p32(rows), self._host_pt_p,
+                                 self.max_rows, self.ld, p64(matched), p64(nodes), p32(new_slots),
+                                 ctypes.byref(done))
+        if rc != rdx.OK:
+            msg = rdx.lib().rdx_last_error().decode()
+            k = done.value  # release the requests admitted before the failure
+            q = (np.diff(offsets) - matched)[:k]
+            off = np.concatenate([[0], np.cumsum(q)]).astype(np.int64)
+            for i in range(k):
+                self.tree.unlock(int(nodes[i]))
+                self.tree.free(new_slots[off[i]:off[i + 1]])
+            self.free_rows.extend(rows[::-1].tolist())
+            raise rdx.RdxError(rc, msg)
+        lens = np.diff(offsets)
+        self._rs.kv_len[rows] = lens
+        self._rs.written[rows] = 0
+        return Batch(self._rs, tokens, offsets, rows, matched, nodes, new_slots)
 
     def _check(self, name, t, rows, heads):
         if (t.device != self.device or t.dtype != self.tdtype or not t.is_contiguous()
@@ -173,8 +214,8 @@ class Runtime:
             raise ValueError(f"{name}: expected contiguous {self.tdtype} [{rows}, {heads}, {self.d}] on "
                              f"{self.device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
 
-    def _launch(self, kind: int, reqs, q_len, new_slots, q, k_new, v_new, o, timer=None):
-        n_new = int(sum(q_len))
+    def _launch(self, kind: int, reqs: Batch, q_len, new_slots, q, k_new, v_new, o, timer=None):
+        n_new = int(np.sum(q_len))
         self._check("q", q, n_new, self.hq)
         self._check("o", o, n_new, self.hq)
         self._check("k_new", k_new, n_new, self.hkv)
@@ -184,8 +225,7 @@ class Runtime:
             plan = rdx.Plan(self.desc, kind, self.plans[kind].target)
         else:
             plan = self.plans[kind]
-        plan.build(self.tree, [r.node for r in reqs], [r.row for r in reqs], [r.kv_len for r in reqs], q_len,
-                   [r.written for r in reqs], new_slots, self.ld)
+        plan.build(self.tree, reqs.nodes, reqs.rows, reqs.kv_len, q_len, reqs.written, new_slots, self.ld)
         info = plan.info()
         self.last_info[kind] = info
         if self.record is not None:
@@ -204,8 +244,7 @@ class Runtime:
             timer[1].record()
         if self.record is not None:
             self.record.append((kind, plan, dev, q, o, info))
-        for r in reqs:
-            r.written = r.kv_len
+        self._rs.written[reqs.rows64] = self._rs.kv_len[reqs.rows64]
         return o
 
     def replay(self, launches, reps: int = 1):
@@ -218,25 +257,23 @@ class Runtime:
                 fn = rdx.extend_attention if kind == rdx.PLAN_EXTEND else rdx.decode_attention
                 fn(self.desc, plan, dev, q, self.k_pool, self.v_pool, self.page_table, o, ws, ws.numel())
 
-    def extend(self, reqs, q, k_new, v_new, o=None, timer=None):
+    def extend(self, reqs: Batch, q, k_new, v_new, o=None, timer=None):
         """Queries q [sum new, Hq, D] and new K/V [sum new, Hkv, D] of the requests' uncached
         tokens, request-major.  Returns o [sum new, Hq, D]."""
-        q_len = [r.kv_len - r.matched for r in reqs]
-        new_slots = np.concatenate([r.new_slots for r in reqs]) if reqs else np.zeros(0, np.int32)
+        q_len = reqs.kv_len - reqs.matched
+        new_slots = reqs.new_slots[: int(reqs.new_off[-1])]
         if o is None:
             o = self.torch.empty_like(q)
         return self._launch(rdx.PLAN_EXTEND, reqs, q_len, new_slots, q, k_new, v_new, o, timer)
 
-    def decode_step(self, reqs, q, k_new, v_new, o=None, timer=None):
+    def decode_step(self, reqs: Batch, q, k_new, v_new, o=None, timer=None):
         """One new token per request: q [R, Hq, D], k_new/v_new [R, Hkv, D].
         One rdx_decode_step call: slot allocation, page-table rows, plan,
         upload, KV scatter and decode attention (timer, if given, brackets
         the whole step)."""
         if self.record is not None:
             return self._decode_step_recorded(reqs, q, k_new, v_new, o, timer)
-        db = self._dec
-        if db is None or not db.matches(reqs):
-            db = self._dec = _DecodeBatch(reqs)
+        db = reqs
         n = db.n
         self._check_step(q, k_new, v_new, o, n)
         if o is None:
@@ -271,31 +308,42 @@ class Runtime:
             if t is not None:
                 self._check(name, t, n, heads)
 
-    def _decode_step_recorded(self, reqs, q, k_new, v_new, o, timer):
-        slots = self.tree.alloc(len(reqs)).copy()
-        rows = np.fromiter((r.row for r in reqs), np.int64, len(reqs))
-        pos = np.fromiter((r.kv_len for r in reqs), np.int64, len(reqs))
-        if pos.size and pos.max() >= self.ld:
+    def _decode_step_recorded(self, reqs: Batch, q, k_new, v_new, o, timer):
+        n = reqs.n
+        pos = self._rs.kv_len[reqs.rows64].astype(np.int64)
+        if n and pos.max() >= self.ld:
             raise RuntimeError("page-table row full")
-        self.host_pt[rows, pos] = slots
-        for r in reqs:
-            r.kv_len += 1
+        slots = self.tree.alloc(n).copy()
+        self.host_pt[reqs.rows64, pos] = slots
+        self._rs.kv_len[reqs.rows64] += 1
         if o is None:
             o = self.torch.empty_like(q)
-        return self._launch(rdx.PLAN_DECODE, reqs, [1] * len(reqs), slots, q, k_new, v_new, o, timer)
+        return self._launch(rdx.PLAN_DECODE, reqs, np.ones(n, np.int32), slots, q, k_new, v_new, o, timer)
 
-    def finish(self, reqs, generated=None):
-        """Insert each request's prompt + generated tokens, free duplicate slots, unlock."""
-        self._dec = None
-        for i, r in enumerate(reqs):
-            gen = np.zeros(0, np.int32) if generated is None else np.asarray(generated[i], np.int32)
-            seq = np.concatenate([r.prompt, gen]).astype(np.int32)
-            if len(seq) != r.kv_len:
-                raise ValueError("generated tokens do not match the request's length")
-            row = self.host_pt[r.row, : r.kv_len]
-            k, _ = self.tree.insert(seq, row)
-            if k > r.matched:
-                self.tree.free(row[r.matched:k])
-            self.tree.unlock(r.node)
-            r._freeze()
-            self.free_rows.append(r.row)
+    def finish(self, reqs: Batch, generated=None, seq=None):
+        """One rdx_finish call: per request, insert prompt + generated tokens
+        with the row's slots, free the duplicates, unlock.  generated: per
+        request the generated token ids (or None); seq: the full sequences
+        already concatenated, as (tokens, offsets)."""
+        kv = reqs.kv_len.astype(np.int64)
+        if seq is not None:
+            tokens, offsets = np.ascontiguousarray(seq[0], np.int32), np.ascontiguousarray(seq[1], np.int64)
+        elif generated is None:
+            tokens, offsets = reqs.tokens, reqs.offsets
+        else:
+            parts = []
+            for i in range(reqs.n):
+                parts.append(reqs.tokens[reqs.offsets[i]:reqs.offsets[i + 1]])
+                parts.append(np.asarray(generated[i], np.int32))
+            tokens = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+            glen = np.array([len(generated[i]) for i in range(reqs.n)], np.int64)
+            offsets = np.concatenate([[0], np.cumsum(reqs.lens + glen)]).astype(np.int64)
+        if len(offsets) != reqs.n + 1 or not np.array_equal(np.diff(offsets), kv):
+            raise ValueError("generated tokens do not match the requests' lengths")
+        done = rdx.i32()
+        p32, p64 = rdx._p32, (lambda x: x.ctypes.data_as(rdx.i64p))
+        rdx._check(rdx.lib().rdx_finish(self.tree.handle, reqs.n, p32(tokens), p64(offsets), p32(reqs.rows),
+                                        self._host_pt_p, self.max_rows, self.ld, p64(reqs.matched),
+                                        p64(reqs.nodes), ctypes.byref(done)))
+        reqs._final = (kv.astype(np.int32), self._rs.written[reqs.rows64].copy())
+        self.free_rows.extend(reqs.rows.tolist())
