@@ -68,36 +68,38 @@ __device__ __forceinline__ void store_out(__bf16* p, float v) { *p = (__bf16)v; 
 //   ws_ml[((kvh * ws_tokens + base + t - lo) * group + hh) * 2 + {0: m, 1: l}]
 // with o already normalised by its own l.  Each workgroup merges 16 query
 // rows of one split tile for one KV head (16 lanes per row, D/16 values per
-// lane), visiting only the contributions that cover the row's token.  It
-// runs after the attention kernel in stream order.
+// lane), visiting only the partials that cover the row's token (the plan
+// lists their workspace tokens per tile token).  It runs after the attention
+// kernel in stream order.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
   constexpr int kPer = D / 16;  // values per lane
-  const int32_t* mb = a.mblocks + (int64_t)(blockIdx.x / a.hkv) * 2;
+  // merge block record: first row, tile token count, tile first token, tile
+  // merge-list base (no tile lookup); merge-list entries are workspace tokens
+  const int32_t* mb = a.mblocks + (int64_t)(blockIdx.x / a.hkv) * kMBlockWords;
   const int kvh = blockIdx.x % a.hkv;
-  const int32_t* tile = a.tiles + (int64_t)mb[0] * kTileWords;
   const int group = a.group;
-  const int row = mb[1] + threadIdx.x / 16;
+  const int row = mb[0] + threadIdx.x / 16;
   const int part = threadIdx.x % 16;
-  const bool live = row < tile[1] * group;  // 16-lane groups stay whole for the shuffles
+  const bool live = row < mb[1] * group;  // 16-lane groups stay whole for the shuffles
   const int t = live ? row / group : 0, hh = live ? row % group : 0;
-  const int32_t* cp = a.cptr + tile[5] + t;
+  const int32_t* cp = a.cptr + mb[3] + t;
   const int cs = live ? cp[0] : 0, n = live ? cp[1] - cp[0] : 0;
+  const int32_t q_index = live ? a.toks[(int64_t)(mb[2] + t) * kTokWords] : 0;
   const int rbase = kvh * (int)a.ws_tokens;
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float wsum = 0.f, mrun = -INFINITY;
-  // contributions in batches of 16: lane `part` fetches (m, l) of one of them,
-  // then the 16 lanes accumulate every contribution's slice of o
+  // partials in batches of 16: lane `part` fetches (m, l) of one of them,
+  // then the 16 lanes accumulate every partial's slice of o
   for (int k0 = 0; k0 < n; k0 += 16) {
     const int k = k0 + part;
     float m = -INFINITY, l = 0.f;
     int w = 0;
     if (k < n) {
-      const int32_t* cr = a.contribs + (int64_t)(tile[3] + a.clist[cs + k]) * kContribWords;
-      w = (rbase + cr[2] + t - cr[0]) * group + hh;
+      w = (rbase + a.clist[cs + k]) * group + hh;
       m = a.ws_ml[(int64_t)w * 2];
       l = a.ws_ml[(int64_t)w * 2 + 1];
     }
@@ -132,7 +134,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
   }
   if (!live) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int32_t q_index = a.toks[(int64_t)(tile[0] + t) * kTokWords];
   T* dst = reinterpret_cast<T*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + hh) * D + part * kPer;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) store_out(dst + e, acc[e] * inv);
@@ -1191,7 +1192,8 @@ __global__ void page_table_write_kernel(int32_t* __restrict__ pt, int64_t ld, co
 // Everything one decode step must write before its attention launch, in one
 // kernel: workgroups [0, n_copy) copy the work list from the mapped host
 // staging buffer to the device plan buffer (16 bytes per thread), the next
-// n_runs each write one page-table run, the rest scatter the new K/V rows.
+// ceil(n_runs / 256) write the page-table runs (one per thread), the rest
+// scatter the new K/V rows.
 // Runs, run slots and new slots are read from the staging buffer too, since
 // the device copy is being written by this same launch.
 __global__ void step_store_kernel(const int4* __restrict__ stage, int4* __restrict__ dev_plan, int64_t n_vec4,
@@ -1206,16 +1208,27 @@ __global__ void step_store_kernel(const int4* __restrict__ stage, int4* __restri
       dev_plan[i] = stage[i];
     return;
   }
-  if (bx < n_copy + n_runs) {
-    const int32_t* r = runs + (int64_t)(bx - n_copy) * kRunWords;
-    int32_t* dst = pt + (int64_t)r[0] * ld + r[1];
-    const int32_t* src = run_slots + r[3];
-    for (int i = threadIdx.x; i < r[2]; i += blockDim.x) dst[i] = src[i];
+  const int32_t n_pt = (n_runs + (int32_t)blockDim.x - 1) / (int32_t)blockDim.x;
+  if (bx < n_copy + n_pt) {
+    // one run per thread.  A decode step's runs are one entry each, in run
+    // order, so the slot is read speculatively next to the run record (two
+    // reads of mapped host memory in parallel instead of one after the
+    // other) and used when the record confirms it.
+    const int32_t ri = (bx - n_copy) * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+    if (ri >= n_runs) return;
+    const int4 r = reinterpret_cast<const int4*>(runs)[ri];  // page row, first position, count, source
+    const int32_t guess = run_slots[ri];  // in bounds: every run has at least one entry
+    int32_t* dst = pt + (int64_t)r.x * ld + r.y;
+    if (r.z == 1 && r.w == ri) {
+      dst[0] = guess;
+    } else {
+      for (int i = 0; i < r.z; ++i) dst[i] = run_slots[r.w + i];
+    }
     return;
   }
   const int64_t total = n * row_vecs;
-  const int64_t nb = (int64_t)gridDim.x - n_copy - n_runs;
-  for (int64_t i = ((int64_t)bx - n_copy - n_runs) * blockDim.x + threadIdx.x; i < total; i += nb * blockDim.x) {
+  const int64_t nb = (int64_t)gridDim.x - n_copy - n_pt;
+  for (int64_t i = ((int64_t)bx - n_copy - n_pt) * blockDim.x + threadIdx.x; i < total; i += nb * blockDim.x) {
     const int64_t tok = i / row_vecs, e = i % row_vecs;
     const int64_t dst = (int64_t)slots[tok] * row_vecs + e;
     kp[dst] = kn[i];

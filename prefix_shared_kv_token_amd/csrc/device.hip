@@ -90,7 +90,7 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   if (!dev_plan || !q || !kp || !vp || !pt || !o) return fail(RDX_EINVAL, "attention: null device pointer");
   if (p->ws_bytes > 0 && (!ws || ws_bytes < p->ws_bytes))
     return fail(RDX_EINVAL, "attention: workspace of %lld bytes needed", (long long)p->ws_bytes);
-  const int64_t n_merge = (int64_t)(p->mblocks.size() / 2) * desc->num_kv_heads;
+  const int64_t n_merge = (int64_t)(p->mblocks.size() / kMBlockWords) * desc->num_kv_heads;
   if (p->ws_tokens * desc->num_q_heads >= ((int64_t)1 << 31))
     return fail(RDX_EUNSUPPORTED, "attention: split workspace too large (%lld partial rows)",
                 (long long)(p->ws_tokens * desc->num_q_heads));
@@ -355,7 +355,8 @@ int rdx_decode_step(rdx_tree* tree, rdx_plan* hplan, const rdx_attn_desc* desc, 
     if (n_copy > 64) n_copy = 64;
     int64_t kv_blocks = (total + 255) / 256;
     if (kv_blocks > 65536) kv_blocks = 65536;
-    hipLaunchKernelGGL(step_store_kernel, dim3((unsigned)(n_copy + n_runs + kv_blocks)), dim3(256), 0, st,
+    const int64_t n_pt = (n_runs + 255) / 256;
+    hipLaunchKernelGGL(step_store_kernel, dim3((unsigned)(n_copy + n_pt + kv_blocks)), dim3(256), 0, st,
                        reinterpret_cast<const int4*>(hs), reinterpret_cast<int4*>(io->dev_plan), n_vec4,
                        (int32_t)n_copy, io->page_table, ld, hs + p->off_runs, hs + p->off_run_slots, (int32_t)n_runs,
                        reinterpret_cast<uint4*>(io->k_pool), reinterpret_cast<uint4*>(io->v_pool),

@@ -338,12 +338,13 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
         cptr.push_back((int32_t)clist.size());
         for (int c = 0; c < (int)mine.size(); ++c) {
           const int32_t* cr = &contribs[(cbase + c) * kContribWords];
-          if (tok >= cr[0] && tok < cr[1]) clist.push_back(c);
+          if (tok >= cr[0] && tok < cr[1]) clist.push_back(cr[2] + tok - cr[0]);  // its workspace token
         }
       }
       cptr.push_back((int32_t)clist.size());
       const int rows = tl[1] * group();
-      for (int r0 = 0; r0 < rows; r0 += kMergeRows) mblocks.insert(mblocks.end(), {t, r0});
+      for (int r0 = 0; r0 < rows; r0 += kMergeRows)
+        mblocks.insert(mblocks.end(), {r0, tl[1], tl[0], tl[5]});
     }
     for (auto& it : mine) {
       its.push_back(it);

@@ -28,6 +28,7 @@ constexpr int kTokWords = 2;      // q_index, position
 constexpr int kContribWords = 4;  // tok_lo, tok_hi, ws_token_base
 constexpr int kRunWords = 4;      // page_row, pos_begin, count, src_offset
 constexpr int kMergeRows = 16;    // query rows per merge workgroup (16 lanes per row)
+constexpr int kMBlockWords = 4;   // first row, tile n_tok, tile tok_begin, tile cptr base
 
 struct Plan {
   rdx_attn_desc desc{};
@@ -35,9 +36,10 @@ struct Plan {
   int32_t target_items = 0;
   int64_t ld = 0;
   // host records
-  // merge of split tiles: per tile token, the contributions covering it
+  // merge of split tiles: per tile token, the partial states covering it
   // (cptr: n_tok + 1 offsets per split tile, tile word 5 = its base; clist:
-  // contribution indices local to the tile), and 16-row merge blocks
+  // the workspace token of each partial), and 16-row merge blocks carrying
+  // the tile fields the merge needs (kMBlockWords)
   std::vector<int32_t> items, tiles, jobs, toks, contribs, runs, run_slots, new_slots, cptr, clist, mblocks;
   int64_t num_split_tiles = 0, num_shared_segments = 0, ws_tokens = 0, key_rows = 0;
   int64_t max_page_row = -1;
