@@ -116,10 +116,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
     mrun = mnew;
     const float wt = l > 0.f ? l * exp2_fast(m - mnew) : 0.f;
     const int cnt = min(16, n - k0);
+    // branch-free body, unrolled by 4, so the partials' reads overlap
+#pragma unroll 4
     for (int j = 0; j < cnt; ++j) {
       const float wj = __shfl(wt, j, 16);
       const int wi = __shfl(w, j, 16);
-      if (wj == 0.f) continue;
       const float4* src = reinterpret_cast<const float4*>(a.ws_o + (int64_t)wi * D + part * kPer);
 #pragma unroll
       for (int e = 0; e < kPer / 4; ++e) {
