@@ -238,8 +238,10 @@ int rdx_plan_upload(rdx_plan* plan, void* dev_plan, int64_t dev_plan_bytes,
 
 /* Host view of a built plan (for tests and tools).  Arrays stay valid until
  * the next rdx_plan_build.  Record layouts are int32:
- *   item    [4] tile, job_begin, job_end, contrib -- one per key chunk; the
- *               launch runs item i for KV head h as workgroup i * Hkv + h
+ *   item    [20] tile, job_begin, job_end, contrib, then copies of what a
+ *               workgroup needs first (block count, tile and contribution
+ *               fields, first job) -- one per key chunk; the launch runs
+ *               item i for KV head h as workgroup i * Hkv + h
  *   tile    [8] tok_begin, n_tok, n_contrib, contrib_begin, counter (-1 = no merge), 0,0,0
  *   job     [8] page_row, key_begin, key_end, tok_lo, tok_hi, causal, 0, 0
  *   token   [2] q_index, position

@@ -790,21 +790,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane & 15, g = lane >> 4;
+  // the item record carries the tile, contribution and first-job fields, so
+  // one read starts the page-table and Q loads (no tile/job/contribution
+  // lookups on the way to the first K/V request)
   const int32_t* item = a.items + (int64_t)(blockIdx.x / (unsigned)a.hkv) * kItemWords;
-  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
   const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
-  const int jb = item[1], je = item[2];
-  const int tok_begin = tile[0], n_tok = tile[1];
+  const int jb = item[1], je = item[2], nblk = item[4];
+  const int tok_begin = item[5], n_tok = item[6];
+  const bool split = item[7] >= 0;
+  const int act_lo = item[8], act_hi = item[9], ws_base = item[10];
   const int group = a.group;
   const int n_rows = n_tok * group;
   const int row = 16 * wave + rr;
   const int tloc = row / group;
-  int act_lo = 0, act_hi = n_tok;
-  if (tile[4] >= 0) {
-    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
-    act_lo = cr0[0];
-    act_hi = cr0[1];
-  }
   const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
   const bool wave_live = __ballot(row_ok) != 0;
 
@@ -828,12 +826,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = a.scale_log2;
 
-  int nblk = 0;
-  for (int j = jb; j < je; ++j) {
-    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
-    nblk += (job[2] - job[1] + 63) >> 6;
-  }
-
   DecPool<D, OFF32> pool;
   pool.init(a);
   const int kk = tid >> 2, cq = tid & 3;  // staging: key row kk, chunks CPT*cq ..
@@ -843,7 +835,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
 
   if (nblk > 0) {
     BlockIter it_s, it_c;
-    iter_job(a, it_s, jb);
+    it_s.j = jb;
+    it_s.prow = a.page_table + (int64_t)item[11] * a.ld;
+    it_s.kb = item[12];
+    it_s.k1 = item[13];
     it_c = it_s;
     DecStage<CPT> r0, r1;
     const uint32_t o0 = pool.offset(slot_of(it_s), in_row);
@@ -857,8 +852,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
     dec_store<D, CPT>(buf[0], r0, kk, cq);
     __syncthreads();
 
-    int cur_job = -1, lim = 0;
-    bool wave_job = false;
+    // the first job's view from the item record
+    int cur_job = jb;
+    int lim = (row_ok && tloc >= item[14] && tloc < item[15]) ? (item[16] ? min(item[13], qpos + 1) : item[13]) : 0;
+    bool wave_job = wave_live && __ballot(lim > item[12]) != 0;
     // block b: compute from buf[b & 1]; the registers of block b+1 are
     // stored behind it; block b+2 is issued into the registers block b used
     // Issue order matters (loads retire in order for the wait counter): the
@@ -892,7 +889,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   // ---- result: rows of this lane (4 lane groups share a row) ----
   const float l_tot = half_swap_sum(row16_swap_sum(l_run));
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (tile[4] < 0) {
+  if (!split) {
     if (row_ok) {
       const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
       __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
@@ -906,9 +903,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
     }
     return;
   }
-  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
-  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
-    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+  if (row_ok) {  // row_ok implies act_lo <= tloc < act_hi
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + ws_base + tloc - act_lo) * group + row % group;
     float* dst = a.ws_o + w * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)

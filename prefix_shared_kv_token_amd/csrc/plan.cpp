@@ -356,7 +356,21 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   std::stable_sort(its.begin(), its.end(), [](const ItemRec& a, const ItemRec& c) { return a.cost > c.cost; });
   // one record per chunk; the launch runs record i for KV heads 0..Hkv-1 as
   // workgroups i*Hkv .. i*Hkv+Hkv-1
-  for (auto& it : its) items.insert(items.end(), {it.tile, it.jb, it.je, it.c});
+  for (auto& it : its) {
+    const int32_t* tl = &tiles[(int64_t)it.tile * kTileWords];
+    int32_t nb = 0;
+    for (int32_t jx = it.jb; jx < it.je; ++jx) nb += (jobs[jx * kJobWords + 2] - jobs[jx * kJobWords + 1] + 63) / 64;
+    int32_t lo = 0, hi = tl[1], base = 0;
+    if (tl[4] >= 0) {
+      const int32_t* cr = &contribs[(int64_t)(tl[3] + it.c) * kContribWords];
+      lo = cr[0];
+      hi = cr[1];
+      base = cr[2];
+    }
+    const int32_t* j0 = &jobs[(int64_t)it.jb * kJobWords];
+    items.insert(items.end(), {it.tile, it.jb, it.je, it.c, nb, tl[0], tl[1], tl[4], lo, hi, base, j0[0], j0[1],
+                               j0[2], j0[3], j0[4], j0[5], 0, 0, 0});
+  }
 
   // ---- workspace ----
   const int64_t hq = desc.num_q_heads, d = desc.head_dim;

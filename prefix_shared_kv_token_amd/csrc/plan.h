@@ -21,7 +21,13 @@ constexpr int kKeyBlock = 64;    // keys per inner iteration of the kernels
 constexpr int kDecodeTileRows = 64;  // query rows per tile of the bf16 decode kernel
 
 // Record layouts (int32 words) -- shared with the device code.
-constexpr int kItemWords = 4;     // tile, job_begin, job_end, contrib (one per key chunk; run for every KV head)
+// item: one per key chunk, run for every KV head.  Words 0-3: tile,
+// job_begin, job_end, contrib (index within the tile); 4: 64-key blocks of
+// the item; 5-7: the tile's tok_begin, n_tok, split index (-1: none); 8-10:
+// the contribution's tok_lo, tok_hi, ws_token_base (0, n_tok, 0 unsplit);
+// 11-16: the first job (page_row, key_begin, key_end, tok_lo, tok_hi,
+// causal) -- everything a workgroup needs to start loading in one read.
+constexpr int kItemWords = 20;
 constexpr int kTileWords = 8;     // tok_begin, n_tok, n_contrib, contrib_begin, split index (-1: none), cptr base
 constexpr int kJobWords = 8;      // page_row, key_begin, key_end, tok_lo, tok_hi, causal
 constexpr int kTokWords = 2;      // q_index, position

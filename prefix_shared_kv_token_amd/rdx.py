@@ -272,7 +272,7 @@ class Plan:
                 return np.zeros((0, w), np.int32)
             return np.ctypeslib.as_array(p, shape=(n * w,)).reshape(n, w).copy()
 
-        return dict(items=arr(v.items, v.num_items, 4), tiles=arr(v.tiles, v.num_tiles, 8),
+        return dict(items=arr(v.items, v.num_items, 20), tiles=arr(v.tiles, v.num_tiles, 8),
                     jobs=arr(v.jobs, v.num_jobs, 8), tokens=arr(v.tokens, v.num_tokens, 2),
                     contribs=arr(v.contribs, v.num_contribs, 4), tile_rows=v.tile_rows, group=v.group)
 
