@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="helpdesk")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--shuffle-seed", type=int, default=None,
+                    help="scattered pool: twice the slots, a seeded random half left free before each step")
     ap.add_argument("--instrumented-steps", type=int, default=1,
                     help="timed steps (the last ones) whose kernels carry timing events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,7 +168,9 @@ def main():
     cfg = config_by_name(args.config)
     wl = Workload(cfg)
     print(f"[bench] {cfg.name}: building inputs", file=sys.stderr, flush=True)
-    run = WorkloadRun(wl, extend_items=args.extend_items, decode_items=args.decode_items)
+    shuffled = args.shuffle_seed is not None
+    run = WorkloadRun(wl, extend_items=args.extend_items, decode_items=args.decode_items,
+                      hole_seed=args.shuffle_seed, extra_slots=cfg.total_tokens() if shuffled else 0)
     # long-lived objects (inputs, torch, the workload) out of the collector's
     # reach, as a serving process does after start-up: a full collection of
     # them would otherwise land inside some step
@@ -259,7 +263,9 @@ def main():
         "data": "synthetic (seeded N(0,1)*sigma Q/K/V, uniform token ids)",
         "config": {"workload": cfg.name, "levels": [list(l) for l in cfg.levels],
                    "decode_steps": cfg.decode_steps, "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
-                   "head_dim": cfg.head_dim, "tokens_per_step": tokens_per_step, "parallelism": "none (1 GPU)"},
+                   "head_dim": cfg.head_dim, "tokens_per_step": tokens_per_step, "parallelism": "none (1 GPU)",
+                   "pool": (f"scattered: 2x slots, random half free (seed {args.shuffle_seed})" if shuffled
+                            else "exact size, ascending free ids")},
         "extend_query_tokens_per_s": member_tokens / ext_member_s,
         "decode_tokens_per_s": cfg.decode_steps * R / dec_total_s if dec_total_s else None,
         "roofline": dominant,

@@ -207,9 +207,10 @@ struct PoolReader {
     r.d = chunk(s.w, off);
     return r;
   }
-  // valid == false: no row is wanted.  With 32-bit offsets the loads get an
-  // offset past the buffer's end and return zeros without a memory access;
-  // otherwise they read the (valid) rows anyway.
+  // valid == false: no row is wanted (the slots may be stale or never
+  // written).  With 32-bit offsets the loads get an offset past the buffer's
+  // end and return zeros without a memory access; otherwise they read row 0,
+  // which always exists.
   __device__ __forceinline__ Rows4 rows_if(const int4& s, uint32_t off, bool valid) const {
     if constexpr (OFF32) {
       auto o = [&](int slot) { return valid ? __umul24((uint32_t)slot, row_bytes) + off : 0x80000000u; };
@@ -224,7 +225,7 @@ struct PoolReader {
       r.d = ld(o(s.w));
       return r;
     } else {
-      return rows(s, off);
+      return rows(valid ? s : make_int4(0, 0, 0, 0), off);
     }
   }
 };

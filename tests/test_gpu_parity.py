@@ -134,6 +134,17 @@ def test_deterministic_and_kv_store_roundtrip():
     np.testing.assert_array_equal(vp, v_log)
 
 
+def test_pool_over_2gib_uses_64bit_addressing():
+    """A KV pool of more than 2 GiB per tensor (32 x 128 bf16 heads, ~264k
+    slots) takes the kernels' 64-bit address path; the scattered free set puts
+    the workload's pages all over it, past the 2 GiB mark."""
+    row_bytes = 32 * 128 * 2
+    extra = (1 << 31) // row_bytes + 4096
+    cfg = config_by_name("helpdesk").replace(levels=((1, 60), (6, 20)), decode_steps=3)
+    run, _, _ = run_and_check(cfg, hole_seed=21, extra_slots=extra)
+    assert run.num_slots * row_bytes > (1 << 31)
+
+
 def test_separate_calls_match_decode_step():
     """The decode path through the separate entry points (rdx_plan_build,
     rdx_plan_upload, rdx_kv_store, rdx_decode_attention; used when launches
