@@ -268,7 +268,10 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     }
   }
   sc.tile_job_begin.push_back((int)sc.tjobs.size());
-  for (const Job& j : sc.tjobs) total_cost += j.k1 - j.k0;
+  // cost unit: 64-key blocks (a block costs about the same whether or not
+  // all its keys exist: the same MFMA work in extend, about one memory round
+  // trip in decode)
+  for (const Job& j : sc.tjobs) total_cost += (j.k1 - j.k0 + kKeyBlock - 1) / kKeyBlock;
 
   // ---- split into items ----
   const int hkv = desc.num_kv_heads;
@@ -281,8 +284,7 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   int64_t chunk = INT64_MAX;
   if ((int64_t)ntiles * hkv < target && total_cost > 0) {
     int64_t per_kvh = std::max<int64_t>(1, target / hkv);
-    chunk = (total_cost + per_kvh - 1) / per_kvh;
-    chunk = std::max<int64_t>(kKeyBlock, (chunk + kKeyBlock - 1) / kKeyBlock * kKeyBlock);
+    chunk = std::max<int64_t>(1, (total_cost + per_kvh - 1) / per_kvh);  // blocks per item
   }
   jobs.clear();
   contribs.clear();
@@ -293,7 +295,7 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   num_split_tiles = 0;
   ws_tokens = 0;
   key_rows = 0;
-  struct ItemRec { int32_t tile, jb, je, c; int64_t cost; };
+  struct ItemRec { int32_t tile, jb, je, c; int64_t cost, keys; };
   static thread_local std::vector<ItemRec> its, mine;
   its.clear();
   for (int t = 0; t < ntiles; ++t) {
@@ -306,15 +308,18 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
         int64_t room = chunk - cur;
         if (room <= 0 || mine.empty()) {
           mine.push_back({t, (int32_t)(jobs.size() / kJobWords), (int32_t)(jobs.size() / kJobWords),
-                          (int32_t)mine.size(), 0});
+                          (int32_t)mine.size(), 0, 0});
           cur = 0;
           room = chunk;
         }
-        int64_t e = room >= (int64_t)j.k1 - a ? (int64_t)j.k1 : a + room;
+        // room is in blocks: the piece takes whole blocks of the job
+        const int64_t e = room >= ((int64_t)j.k1 - a + kKeyBlock - 1) / kKeyBlock ? (int64_t)j.k1 : a + room * kKeyBlock;
+        const int64_t nb = (e - a + kKeyBlock - 1) / kKeyBlock;
         jobs.insert(jobs.end(), {j.row, (int32_t)a, (int32_t)e, j.lo, j.hi, j.causal, 0, 0});
         mine.back().je++;
-        mine.back().cost += e - a;
-        cur += e - a;
+        mine.back().cost += nb;
+        mine.back().keys += e - a;
+        cur += nb;
         a = e;
       }
     }
@@ -348,7 +353,7 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     }
     for (auto& it : mine) {
       its.push_back(it);
-      key_rows += it.cost * (int64_t)tl[1] * group();
+      key_rows += it.keys * (int64_t)tl[1] * group();
     }
   }
   key_rows *= hkv;
