@@ -75,8 +75,10 @@ __device__ __forceinline__ void store_out(__bf16* p, float v) { *p = (__bf16)v; 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
   constexpr int kPer = D / 16;  // values per lane
-  // merge block record: first row, tile token count, tile first token, tile
-  // merge-list base (no tile lookup); merge-list entries are workspace tokens
+  constexpr int kV4 = kPer / 4;
+  // merge block record: first row, tile token count, tile first token, the
+  // block's first tile token and its tokens' merge-list offsets (no tile or
+  // offset lookups); merge-list entries are workspace tokens
   const int32_t* mb = a.mblocks + (int64_t)(blockIdx.x / a.hkv) * kMBlockWords;
   const int kvh = blockIdx.x % a.hkv;
   const int group = a.group;
@@ -84,24 +86,34 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
   const int part = threadIdx.x % 16;
   const bool live = row < mb[1] * group;  // 16-lane groups stay whole for the shuffles
   const int t = live ? row / group : 0, hh = live ? row % group : 0;
-  const int32_t* cp = a.cptr + mb[3] + t;
-  const int cs = live ? cp[0] : 0, n = live ? cp[1] - cp[0] : 0;
+  const int lt = live ? t - mb[3] : 0;
+  const int cs = live ? mb[4 + lt] : 0, n = live ? mb[5 + lt] - cs : 0;
   const int32_t q_index = live ? a.toks[(int64_t)(mb[2] + t) * kTokWords] : 0;
   const int rbase = kvh * (int)a.ws_tokens;
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float wsum = 0.f, mrun = -INFINITY;
-  // partials in batches of 16: lane `part` fetches (m, l) of one of them,
-  // then the 16 lanes accumulate every partial's slice of o
+  // partials in batches of 16: once the list entries are in, lane `part`
+  // reads (m, l) of one partial while every lane reads its slice of o of all
+  // of them -- one round trip -- and then the weights are formed and applied
   for (int k0 = 0; k0 < n; k0 += 16) {
     const int k = k0 + part;
-    float m = -INFINITY, l = 0.f;
+    const int cnt = min(16, n - k0);
     int w = 0;
+    if (k < n) w = (rbase + a.clist[cs + k]) * group + hh;
+    float m = -INFINITY, l = 0.f;
     if (k < n) {
-      w = (rbase + a.clist[cs + k]) * group + hh;
       m = a.ws_ml[(int64_t)w * 2];
       l = a.ws_ml[(int64_t)w * 2 + 1];
+    }
+    float4 ov[16][kV4];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int wj = __shfl(w, j, 16);
+      const float4* src = reinterpret_cast<const float4*>(a.ws_o + (int64_t)wj * D + part * kPer);
+#pragma unroll
+      for (int e = 0; e < kV4; ++e) ov[j][e] = j < cnt ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float bm = l > 0.f ? m : -INFINITY;
 #pragma unroll
@@ -115,20 +127,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
     }
     mrun = mnew;
     const float wt = l > 0.f ? l * exp2_fast(m - mnew) : 0.f;
-    const int cnt = min(16, n - k0);
-    // branch-free body, unrolled by 4, so the partials' reads overlap
-#pragma unroll 4
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __shfl(wt, j, 16);
-      const int wi = __shfl(w, j, 16);
-      const float4* src = reinterpret_cast<const float4*>(a.ws_o + (int64_t)wi * D + part * kPer);
 #pragma unroll
-      for (int e = 0; e < kPer / 4; ++e) {
-        const float4 v = src[e];
-        acc[4 * e] += wj * v.x;
-        acc[4 * e + 1] += wj * v.y;
-        acc[4 * e + 2] += wj * v.z;
-        acc[4 * e + 3] += wj * v.w;
+    for (int j = 0; j < 16; ++j) {
+      const float wj = __shfl(wt, j, 16);
+#pragma unroll
+      for (int e = 0; e < kV4; ++e) {
+        acc[4 * e] += wj * ov[j][e].x;
+        acc[4 * e + 1] += wj * ov[j][e].y;
+        acc[4 * e + 2] += wj * ov[j][e].z;
+        acc[4 * e + 3] += wj * ov[j][e].w;
       }
       wsum += wj;
     }

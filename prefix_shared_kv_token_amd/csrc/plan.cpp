@@ -348,8 +348,12 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
       }
       cptr.push_back((int32_t)clist.size());
       const int rows = tl[1] * group();
-      for (int r0 = 0; r0 < rows; r0 += kMergeRows)
-        mblocks.insert(mblocks.end(), {r0, tl[1], tl[0], tl[5]});
+      for (int r0 = 0; r0 < rows; r0 += kMergeRows) {
+        const int t0 = r0 / group();
+        int32_t rec[kMBlockWords] = {r0, tl[1], tl[0], t0};
+        for (int i = 0; i <= kMergeRows; ++i) rec[4 + i] = cptr[tl[5] + std::min(t0 + i, (int)tl[1])];
+        mblocks.insert(mblocks.end(), rec, rec + kMBlockWords);
+      }
     }
     for (auto& it : mine) {
       its.push_back(it);

@@ -34,7 +34,10 @@ constexpr int kTokWords = 2;      // q_index, position
 constexpr int kContribWords = 4;  // tok_lo, tok_hi, ws_token_base
 constexpr int kRunWords = 4;      // page_row, pos_begin, count, src_offset
 constexpr int kMergeRows = 16;    // query rows per merge workgroup (16 lanes per row)
-constexpr int kMBlockWords = 4;   // first row, tile n_tok, tile tok_begin, tile cptr base
+// merge block: first row, tile n_tok, tile tok_begin, first tile token t0 of
+// the block, then the merge-list offsets (cptr) of tile tokens t0 .. t0+16
+// (clamped to the tile's n_tok), padding
+constexpr int kMBlockWords = 24;
 
 struct Plan {
   rdx_attn_desc desc{};
