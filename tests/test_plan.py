@@ -139,3 +139,30 @@ def test_empty_batch_and_zero_query_requests():
     s = tree.alloc(3)
     plan.build(tree, [0, 0], [0, 1], [3, 0], [3, 0], [0, 0], s, 8)
     assert plan.info()["num_new"] == 3 and plan.info()["num_tiles"] == 1
+
+
+def test_decode_items_are_sized_in_blocks():
+    """Work items are cut in 64-key blocks, not keys: items made of many short
+    own-suffix jobs carry no more blocks than items cut from a long shared
+    prefix (the longest item sets the launch's end), and cuts fall on block
+    boundaries (no block is split between items)."""
+    cfg = config_by_name("helpdesk").replace(levels=((1, 1000), (64, 40)), decode_steps=1, n_q_heads=8,
+                                             n_kv_heads=2)
+    wl, tree, phases = _admit_phases(cfg)
+    reqs = phases[-1]
+    desc = rdx.attn_desc(rdx.BF16, 8, 2, 128, cfg.total_tokens())
+    rows = list(range(len(reqs)))
+    kv = [len(p) + 101 for p, *_ in reqs]  # decode step 100: 141 own keys (3 blocks) per request
+    target = 32  # 16 records per KV head
+    plan = rdx.Plan(desc, rdx.PLAN_DECODE, target)
+    plan.build(tree, [n for _, _, n, _ in reqs], rows, kv, [1] * len(reqs), [k - 1 for k in kv],
+               tree.alloc(len(reqs)), cfg.max_seq_len + 128)
+    v = plan.view()
+    job_blocks = [(j[2] - j[1] + 63) // 64 for j in v["jobs"]]
+    total = sum(job_blocks)
+    # the 1000 shared keys once per decode tile (16 tokens x 4 grouped heads) + 3 blocks per own suffix
+    assert len(v["tiles"]) == 4 and total == 4 * 16 + 64 * 3
+    per_item = [sum(job_blocks[it[1]:it[2]]) for it in v["items"]]
+    assert [int(it[4]) for it in v["items"]] == per_item
+    assert max(per_item) <= -(-total // (target // 2))
+    assert sum(per_item) == total
