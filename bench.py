@@ -126,6 +126,64 @@ def cpu_baseline(wl, seconds: float):
                       f"BLAS threads = host cores; cpu: {cpu}"}
 
 
+def _serve_in_order(rdx, tree, prompts, order) -> int:
+    """Serves the prompts one after another on `tree` (match, lock, allocate
+    the rest, insert, free duplicates, unlock) -> cached prompt tokens."""
+    cached = 0
+    for i in order:
+        p = prompts[i]
+        m, slots, node = tree.match_prefix(p)
+        if node:
+            tree.lock(node)
+        new = tree.alloc(len(p) - m)
+        k, _ = tree.insert(p, list(slots) + list(new))
+        if k > m:
+            tree.free(new[: k - m])
+        if node:
+            tree.unlock(node)
+        cached += m
+    return cached
+
+
+def schedule_probe(rdx, window: int = 128, reps: int = 20):
+    """Cache-aware ordering (host): one window of `window` waiting requests,
+    leaf prompts of the BatchLLM-shaped workload (prefix 2,000 shared by 16,
+    suffix 200) in a seeded random arrival order, served one at a time on the
+    C++ tree in arrival order and in the rdx_schedule order, with a pool of
+    twice the longest prompt (tight) and one holding the whole window
+    (roomy).  The hit rate is cached prompt tokens / prompt tokens; `optimum`
+    is 1 - (distinct prefixes of the window) / (prompt tokens), what a
+    depth-first order reaches once the pool holds the longest prompt."""
+    import numpy as np
+    from workloads import Workload, config_by_name, waiting_queue
+
+    wl = Workload(config_by_name("batchllm"))
+    prompts = waiting_queue(wl, window)
+    n = len(prompts)
+    total = sum(len(p) for p in prompts)
+    longest = max(len(p) for p in prompts)
+    everything = rdx.Tree(total)
+    _serve_in_order(rdx, everything, prompts, range(n))
+    distinct = everything.stats()["cached"]
+    out = {"queue": f"{n} leaf prompts of batchllm (2000 shared by 16 + 200), seeded random arrival",
+           "prompt_tokens": total, "optimum": 1.0 - distinct / total}
+    for name, cap in (("tight", 2 * longest), ("roomy", total)):
+        fcfs = _serve_in_order(rdx, rdx.Tree(cap), prompts, range(n))
+        tree = rdx.Tree(cap)
+        order, _ = tree.schedule(prompts)
+        lpm = _serve_in_order(rdx, tree, prompts, [int(i) for i in order])
+        out[name] = {"pool_slots": cap, "hit_rate_fcfs": fcfs / total, "hit_rate_lpm": lpm / total}
+    # cost of one ordering call against a tree that holds the whole window
+    # (every prompt's match walks its full length)
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        everything.schedule(prompts)
+        ts.append(time.perf_counter() - t0)
+    out["schedule_us"] = float(np.median(ts) * 1e6)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +196,7 @@ def main():
     ap.add_argument("--instrumented-steps", type=int, default=1,
                     help="timed steps (the last ones) whose kernels carry timing events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-schedule-probe", action="store_true")
     ap.add_argument("--extend-items", type=int, default=0)
     ap.add_argument("--decode-items", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -272,6 +331,9 @@ def main():
         "extend_roofline": extend_roof,
         "decode_roofline": decode_roof,
     }
+    if not args.no_schedule_probe:
+        print("[bench] request ordering on the host tree", file=sys.stderr, flush=True)
+        line["schedule"] = schedule_probe(rdx)
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

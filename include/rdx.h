@@ -133,6 +133,22 @@ int rdx_finish(rdx_tree* tree, int32_t num_reqs, const int32_t* tokens, const in
                const int32_t* rows, const int32_t* host_page_table, int64_t num_rows, int64_t ld,
                const int64_t* matched, const int64_t* node, int32_t* out_done);
 
+/* Cache-aware ordering of the waiting requests (SGLang paper notes,
+ * section 3 "cache-aware scheduling" and appendix A.2; vLLM-vs-SGLang page,
+ * cache-aware ordering).  Request i's prompt is tokens[offsets[i] ..
+ * offsets[i+1]), requests listed in arrival order.  Writes a permutation of
+ * 0..num_reqs-1 to out_order: greedily, the next request is the one whose
+ * prompt shares the longest prefix with the tree or with a request already
+ * placed ahead of it in this order (its tokens will be cached when the later
+ * one runs); ties go to the earliest arrival; shared lengths count whole
+ * matching units.  out_score[k] = that shared length of request out_order[k]
+ * when it was placed.  With more than fcfs_above requests: arrival order and
+ * zero scores, no matching (the queue-length cut-off of the vLLM-vs-SGLang
+ * page; 128 there).  The tree is only read -- no split, no LRU stamp.
+ * Errors: EINVAL (null array, negative count, decreasing offsets). */
+int rdx_schedule(const rdx_tree* tree, int32_t num_reqs, const int32_t* tokens, const int64_t* offsets,
+                 int32_t fcfs_above, int32_t* out_order, int64_t* out_score);
+
 typedef struct rdx_stats {
   int64_t num_slots;
   int64_t free;      /* slots in the free set */

@@ -61,14 +61,30 @@ int64_t RadixTree::walk(const int32_t* t, int64_t n, std::vector<WalkStep>* step
     auto it = cur->children.find(t[m]);
     if (it == cur->children.end()) break;
     Node* c = it->second;
-    int64_t len = (int64_t)c->key.size(), l = 0;
-    while (l < len && m + l < n && c->key[l] == t[m + l]) ++l;
+    const int64_t len = (int64_t)c->key.size();
+    const int64_t l = common_prefix(c->key.data(), t + m, std::min(len, n - m));
     steps->push_back({c, l});
     m += l;
     if (l < len) break;
     cur = c;
   }
   return m;
+}
+
+int64_t RadixTree::peek_match(const int32_t* t, int64_t n) const {
+  const Node* cur = &root_;
+  int64_t m = 0;
+  while (m < n) {
+    auto it = cur->children.find(t[m]);
+    if (it == cur->children.end()) break;
+    const Node* c = it->second;
+    const int64_t len = (int64_t)c->key.size();
+    const int64_t l = common_prefix(c->key.data(), t + m, std::min(len, n - m));
+    m += l;
+    if (l < len) break;
+    cur = c;
+  }
+  return (m / unit_) * unit_;
 }
 
 Node* RadixTree::split(Node* x, int64_t c) {

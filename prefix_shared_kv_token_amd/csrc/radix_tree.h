@@ -9,12 +9,23 @@
 #pragma once
 
 #include <cstdint>
+#include <cstring>
 #include <memory>
 #include <queue>
 #include <unordered_map>
 #include <vector>
 
 namespace rdx {
+
+// Length of the common prefix of a[0..n) and b[0..n): equal 16-token blocks
+// are skipped with memcmp, the first unequal block is scanned.
+inline int64_t common_prefix(const int32_t* a, const int32_t* b, int64_t n) {
+  constexpr int64_t kBlock = 16;
+  int64_t i = 0;
+  while (i + kBlock <= n && std::memcmp(a + i, b + i, kBlock * sizeof(int32_t)) == 0) i += kBlock;
+  while (i < n && a[i] == b[i]) ++i;
+  return i;
+}
 
 struct Node {
   int64_t id = 0;
@@ -40,6 +51,9 @@ class RadixTree {
 
   int match_prefix(const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* out_len,
                    int64_t* out_node);
+  // Matched length rounded down to the matching unit, leaving the tree as it
+  // is (no split, no clock tick): what ordering decisions look at.
+  int64_t peek_match(const int32_t* tokens, int64_t n) const;
   int lock(int64_t node);
   int unlock(int64_t node);
   int alloc(int64_t n, int32_t* out);
@@ -48,6 +62,7 @@ class RadixTree {
              int64_t* out_node);
   int evict(int64_t n_tokens, int64_t* out_freed);
 
+  int32_t match_unit() const { return unit_; }
   int64_t num_slots() const { return num_slots_; }
   int64_t num_free() const { return n_free_; }
   int64_t num_nodes() const { return (int64_t)nodes_.size(); }

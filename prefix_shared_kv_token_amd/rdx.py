@@ -79,6 +79,7 @@ _SIGS = {
     "rdx_evict": (ctypes.c_int, [vp, i64, i64p]),
     "rdx_admit": (ctypes.c_int, [vp, i32, i32p, i64p, i32p, i32p, i64, i64, i64p, i64p, i32p, i32p]),
     "rdx_finish": (ctypes.c_int, [vp, i32, i32p, i64p, i32p, i32p, i64, i64, i64p, i64p, i32p]),
+    "rdx_schedule": (ctypes.c_int, [vp, i32, i32p, i64p, i32, i32p, i64p]),
     "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
     "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
     "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),
@@ -207,6 +208,22 @@ class Tree:
         f = i64()
         _check(lib().rdx_evict(self._h, n_tokens, ctypes.byref(f)))
         return f.value
+
+    def schedule(self, prompts, fcfs_above: int = 128):
+        """Cache-aware order of the waiting `prompts` (arrival order) ->
+        (order, score of each request when placed), both numpy arrays."""
+        n = len(prompts)
+        offsets = np.zeros(n + 1, np.int64)
+        if n:
+            np.cumsum([len(p) for p in prompts], out=offsets[1:])
+        flat = _i32(np.concatenate([np.asarray(p, np.int32).ravel() for p in prompts]) if n else [])
+        if flat.size == 0:
+            flat = np.zeros(1, np.int32)
+        order = np.empty(max(1, n), np.int32)
+        score = np.empty(max(1, n), np.int64)
+        _check(lib().rdx_schedule(self._h, n, _p32(flat), offsets.ctypes.data_as(i64p), fcfs_above,
+                                  _p32(order), score.ctypes.data_as(i64p)))
+        return order[:n], score[:n]
 
     def stats(self) -> dict:
         s = Stats()

@@ -166,6 +166,12 @@ class Runtime:
         return self.workspace
 
     # ------------------------------------------------------------ protocol
+    def schedule(self, prompts, fcfs_above: int = 128) -> np.ndarray:
+        """Cache-aware order of the waiting prompts (arrival order in): the
+        order to admit them in, longest prefix shared with the tree or with a
+        request placed ahead first; arrival order above `fcfs_above`."""
+        return self.tree.schedule(prompts, fcfs_above)[0]
+
     def admit(self, prompts) -> Batch:
         """Admit a list of prompts (token id arrays) as one batch."""
         prompts = [np.asarray(p, np.int32) for p in prompts]
