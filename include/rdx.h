@@ -47,7 +47,7 @@ extern "C" {
 #define RDX_ESTATE (-3)       /* unknown node, refcount underflow, slot not private */
 #define RDX_EUNSUPPORTED (-4) /* dtype / head_dim / head ratio not built */
 #define RDX_EDEVICE (-5)      /* a HIP call failed */
-#define RDX_ENOBUFS (-6)      /* a caller device buffer is too small (sizes reported) */
+#define RDX_ENOBUFS (-6)      /* a caller buffer is too small (sizes reported) */
 
 const char* rdx_last_error(void);
 const char* rdx_version(void);
@@ -148,6 +148,47 @@ int rdx_finish(rdx_tree* tree, int32_t num_reqs, const int32_t* tokens, const in
  * Errors: EINVAL (null array, negative count, decreasing offsets). */
 int rdx_schedule(const rdx_tree* tree, int32_t num_reqs, const int32_t* tokens, const int64_t* offsets,
                  int32_t fcfs_above, int32_t* out_order, int64_t* out_score);
+
+/* Throughput-oriented token batching (BatchLLM explainer: Throughput-oriented
+ * Token Batching, Equations 3-4; three-queue fetching; Memory-centric Token
+ * Batching).  A job of num_groups groups: group g has a common prefix of
+ * prefix_len[g] >= 0 tokens and members member_offsets[g] ..
+ * member_offsets[g+1]-1 (member_offsets[0] = 0, at least one member per
+ * group); member m has a distinct prompt of distinct_len[m] >= 1 tokens and
+ * generates decode_len[m] >= 0 tokens.  Groups run in descending
+ * R_group = 1 / (prefix + sum of distinct prompts), ties by index.  Each
+ * rdx_batcher_next call is one iteration: one DECODE entry per request
+ * decoding (in group order, then member order), then prefill chunks of
+ * min(s_chunk, remaining) tokens in queue order -- DISTINCT chunks of
+ * members whose group prefix was completed in an earlier iteration, then
+ * PREFIX chunks of groups not yet prefilled, one chunk per item -- stopping
+ * at the first chunk that would take the memory above m_threshold; memory =
+ * 2 x (context of every decoding request before its token: prefix +
+ * distinct + generated) + 2 x (chunk tokens taken).  A member decodes from
+ * the iteration after its prompt completes; its t-th token sits at
+ * position prefix + distinct + t.  Needs m_threshold >= 2 s_chunk (an
+ * iteration with nothing decoding always takes a chunk).  The arrays are
+ * copied; errors: EINVAL. */
+#define RDX_TB_DECODE 0
+#define RDX_TB_DISTINCT 1
+#define RDX_TB_PREFIX 2
+typedef struct rdx_batcher rdx_batcher;
+typedef struct rdx_tb_entry {
+  int32_t kind;   /* RDX_TB_DECODE, RDX_TB_DISTINCT or RDX_TB_PREFIX */
+  int32_t group;  /* group index */
+  int32_t member; /* member index (global), -1 for PREFIX */
+  int32_t begin;  /* position of the first token in its sequence */
+  int32_t count;  /* tokens (1 for DECODE) */
+} rdx_tb_entry;
+int rdx_batcher_create(int32_t num_groups, const int32_t* prefix_len, const int32_t* member_offsets,
+                       const int32_t* distinct_len, const int32_t* decode_len, int32_t s_chunk,
+                       int64_t m_threshold, rdx_batcher** out);
+void rdx_batcher_destroy(rdx_batcher* batcher);
+/* Next iteration's entries into out[0 .. *out_n) (decode entries first);
+ * *out_n = 0 once every token of the job has been emitted.  If cap is too
+ * small: RDX_ENOBUFS with *out_n = the entries needed and no state change
+ * (members + groups entries always suffice). */
+int rdx_batcher_next(rdx_batcher* batcher, rdx_tb_entry* out, int32_t cap, int32_t* out_n);
 
 typedef struct rdx_stats {
   int64_t num_slots;

@@ -65,6 +65,10 @@ class StepIO(ctypes.Structure):
                 ("q", vp), ("k_new", vp), ("v_new", vp), ("o", vp)]
 
 
+class TbEntry(ctypes.Structure):
+    _fields_ = [("kind", i32), ("group", i32), ("member", i32), ("begin", i32), ("count", i32)]
+
+
 _SIGS = {
     "rdx_last_error": (ctypes.c_char_p, []),
     "rdx_version": (ctypes.c_char_p, []),
@@ -80,6 +84,9 @@ _SIGS = {
     "rdx_admit": (ctypes.c_int, [vp, i32, i32p, i64p, i32p, i32p, i64, i64, i64p, i64p, i32p, i32p]),
     "rdx_finish": (ctypes.c_int, [vp, i32, i32p, i64p, i32p, i32p, i64, i64, i64p, i64p, i32p]),
     "rdx_schedule": (ctypes.c_int, [vp, i32, i32p, i64p, i32, i32p, i64p]),
+    "rdx_batcher_create": (ctypes.c_int, [i32, i32p, i32p, i32p, i32p, i32, i64, ctypes.POINTER(vp)]),
+    "rdx_batcher_destroy": (None, [vp]),
+    "rdx_batcher_next": (ctypes.c_int, [vp, vp, i32, i32p]),
     "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
     "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
     "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),
@@ -238,6 +245,39 @@ class Tree:
         d = {n: getattr(info, n) for n, _ in NodeInfo._fields_}
         d["slots"] = slots[: info.length].copy()
         return d
+
+
+# ------------------------------------------------------------------ batcher
+TB_DECODE, TB_DISTINCT, TB_PREFIX = 0, 1, 2
+
+
+class Batcher:
+    """rdx_batcher: throughput-oriented token batching of a job of groups
+    (prefix length, members' distinct prompt and decode lengths)."""
+
+    def __init__(self, prefix_len, member_offsets, distinct_len, decode_len, s_chunk: int, m_threshold: int):
+        pl, mo, dl, dc = _i32(prefix_len), _i32(member_offsets), _i32(distinct_len), _i32(decode_len)
+        self._keep = (pl, mo, dl, dc)
+        h = vp()
+        _check(lib().rdx_batcher_create(len(pl), _p32(pl), _p32(mo), _p32(dl) if len(dl) else None,
+                                        _p32(dc) if len(dc) else None, s_chunk, m_threshold, ctypes.byref(h)))
+        self._h = h
+        self._cap = len(dl) + len(pl) + 1
+        self._buf = np.zeros((self._cap, 5), np.int32)
+        self._n = i32()
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.rdx_batcher_destroy(h)
+            self._h = None
+
+    def next(self) -> np.ndarray:
+        """The next iteration's entries, int32 [n, 5] rows (kind, group,
+        member, begin, count); empty once the job is done.  A view of an
+        internal buffer, valid until the next call."""
+        _check(lib().rdx_batcher_next(self._h, self._buf.ctypes.data, self._cap, ctypes.byref(self._n)))
+        return self._buf[: self._n.value]
 
 
 # --------------------------------------------------------------------- plan
