@@ -60,6 +60,119 @@ def decode_bytes(wl, t):
     return kv + qo + 4 * rows
 
 
+def mixed_launch_work(run, e):
+    """(flops, bytes) of one mixed launch, algorithmic: every query token
+    attends to positions 0..p of its sequence (4 D Hq per visible key); the
+    bytes read every distinct KV row the launch needs once (a group's prefix
+    once, each request's own rows once; K and V, plus the 4-byte page
+    index), the queries and the outputs."""
+    import numpy as np
+
+    cfg = run.cfg
+    b = 2 if cfg.dtype == "bf16" else 4
+    kind, grp, begin, cnt = e[:, 0], e[:, 1], e[:, 3].astype(np.int64), e[:, 4].astype(np.int64)
+    end = begin + cnt
+    pairs = int((cnt * begin + cnt * (cnt + 1) // 2).sum())
+    flops = 4 * cfg.head_dim * cfg.n_q_heads * pairs
+    lp = run.prefix_len[grp].astype(np.int64)
+    is_pre = kind == 2
+    # prefix rows per group: the whole prefix when a member of the group is in
+    # the launch, else as far as the group's prefix chunk reaches
+    rows = 0
+    for g in np.unique(grp):
+        sel = grp == g
+        if (~is_pre[sel]).any():
+            rows += int(lp[sel][0])
+        else:
+            rows += int(end[sel].max())
+    rows += int((end - lp)[~is_pre].sum())
+    n_q = int(cnt.sum())
+    nbytes = rows * (2 * cfg.n_kv_heads * cfg.head_dim * b + 4) + 2 * n_q * cfg.n_q_heads * cfg.head_dim * b
+    return flops, nbytes
+
+
+def run_mixed_bench(args, cfg, wl):
+    """The token-batched job: one step = the whole job (every prefix, prompt
+    and decode token of the workload, in the batcher's iterations)."""
+    import numpy as np
+    import torch
+    from prefix_shared_kv_token_amd import rdx
+    from prefix_shared_kv_token_amd.mixed import MixedRun
+    from workloads import decode_lengths
+
+    tlen = decode_lengths(wl)
+    total = cfg.total_tokens() - (cfg.decode_steps * len(wl.leaf_requests) - int(tlen.sum()))
+    m = args.m_threshold or 2 * (total // 5)
+    print(f"[bench] mixed {cfg.name}: s_chunk {args.s_chunk}, M {m}: staging", file=sys.stderr, flush=True)
+    run = MixedRun(wl, args.s_chunk, m, tlen, items=args.extend_items)
+    n_it = len(run.iterations)
+    gc.collect()
+    gc.freeze()
+    for _ in range(args.warmup):
+        run.run()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} jobs of {n_it} launches", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if i == args.steps - 1:
+            rdx.timing_begin(n_it)
+        run.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn_ms, merge_ms, _ = rdx.timing_read(n_it)
+    assert len(attn_ms) == n_it, (len(attn_ms), n_it)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    work = [mixed_launch_work(run, e) for e in run.iterations]
+    flops = np.array([w[0] for w in work], np.float64)
+    nbytes = np.array([w[1] for w in work], np.float64)
+    dur = (attn_ms.astype(np.float64) + merge_ms) / 1e3
+    kinds = [set(e[:, 0].tolist()) for e in run.iterations]
+    dec_only = np.array([k == {0} for k in kinds])
+    has_dec = np.array([0 in k for k in kinds])
+    mixed = has_dec & ~dec_only
+    peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    def roof(sel, bound):
+        d = dur[sel].sum()
+        if bound == "mfma":
+            a = flops[sel].sum() / d / 1e12
+            return {"bound": "mfma", "achieved": a, "peak": peak_tf, "unit": "TFLOP/s", "frac": a / peak_tf,
+                    "traffic": None, "launches": int(sel.sum()), "avg_launch_us": d / max(1, sel.sum()) * 1e6}
+        a = nbytes[sel].sum() / d / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": a / PEAK_HBM_GBS,
+                "traffic": None, "launches": int(sel.sum()), "avg_launch_us": d / max(1, sel.sum()) * 1e6}
+
+    every = np.ones(n_it, bool)
+    prefill_heavy = ~dec_only
+    roof_all = {"mfma": roof(every, "mfma"), "hbm": roof(every, "hbm")}
+    dominant = max(roof_all.values(), key=lambda r: r["frac"])
+    line = {
+        "metric": "mixed extend+decode tokens/s (token-batched job), 1 MI355X",
+        "value": run.n_tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1)*sigma Q/K/V, uniform token ids, output lengths uniform in [1, T])",
+        "config": {"workload": f"{cfg.name} token-batched", "levels": [list(l) for l in cfg.levels],
+                   "max_decode": cfg.decode_steps, "s_chunk": args.s_chunk, "m_threshold": m,
+                   "job_tokens": run.n_tokens, "launches": n_it, "mixed_launches": int(mixed.sum()),
+                   "decode_only_launches": int(dec_only.sum()), "parallelism": "none (1 GPU)"},
+        "roofline": dict(dominant, kernel="extend attention over the mixed batches (all launches)"),
+        "roofline_mfma_all": roof_all["mfma"],
+        "roofline_hbm_all": roof_all["hbm"],
+        "roofline_mfma_with_prefill": roof(prefill_heavy, "mfma") if prefill_heavy.any() else None,
+        "roofline_hbm_decode_only": roof(dec_only, "hbm") if dec_only.any() else None,
+        "attention_ms_per_job": float(dur.sum() * 1e3),
+    }
+    print(json.dumps(line, default=float), flush=True)
+
+
 def kernel_source_digest() -> str:
     """sha256 over the kernel sources and the planner that shapes their
     launches; a counter summary taken from other sources does not apply."""
@@ -197,6 +310,11 @@ def main():
                     help="timed steps (the last ones) whose kernels carry timing events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule-probe", action="store_true")
+    ap.add_argument("--mixed", action="store_true",
+                    help="token-batched job: prefill chunks and decode tokens share each launch")
+    ap.add_argument("--s-chunk", type=int, default=512)
+    ap.add_argument("--m-threshold", type=int, default=0,
+                    help="KV memory bound in K/V entries (default: a fifth of the job's)")
     ap.add_argument("--extend-items", type=int, default=0)
     ap.add_argument("--decode-items", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -226,6 +344,8 @@ def main():
 
     cfg = config_by_name(args.config)
     wl = Workload(cfg)
+    if args.mixed:
+        return run_mixed_bench(args, cfg, wl)
     print(f"[bench] {cfg.name}: building inputs", file=sys.stderr, flush=True)
     shuffled = args.shuffle_seed is not None
     run = WorkloadRun(wl, extend_items=args.extend_items, decode_items=args.decode_items,

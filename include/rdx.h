@@ -163,8 +163,9 @@ int rdx_schedule(const rdx_tree* tree, int32_t num_reqs, const int32_t* tokens, 
  * members whose group prefix was completed in an earlier iteration, then
  * PREFIX chunks of groups not yet prefilled, one chunk per item -- stopping
  * at the first chunk that would take the memory above m_threshold; memory =
- * 2 x (context of every decoding request before its token: prefix +
- * distinct + generated) + 2 x (chunk tokens taken).  A member decodes from
+ * 2 x (the prefix of every group with a decoding request, once) + 2 x (each
+ * decoding request's distinct prompt + tokens generated before this
+ * iteration) + 2 x (chunk tokens taken).  A member decodes from
  * the iteration after its prompt completes; its t-th token sits at
  * position prefix + distinct + t.  Needs m_threshold >= 2 s_chunk (an
  * iteration with nothing decoding always takes a chunk).  The arrays are

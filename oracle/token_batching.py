@@ -19,10 +19,12 @@ Passages followed (BatchLLM explainer):
 Readings of points the pages leave open (the product follows the same):
   * R_group = 1 / (L_prefix + sum of L_distinct) as printed: groups run in
     ascending order of prefill tokens, ties by group index;
-  * kv_memory of a decoding request = 2 x its context before this
-    iteration's token (common prefix + distinct prompt + tokens generated so
-    far); decode tokens are always taken and add no memory in that
-    iteration (as in the sketch); requests still in prefill are not counted;
+  * the decoding requests' KV memory counts what they hold: a group's common
+    prefix once (it is shared, the point of prefix sharing), plus each
+    decoding request's distinct prompt and the tokens it generated so far,
+    before this iteration's token; decode tokens are always taken and add no
+    memory in that iteration (as in the sketch); requests still in prefill
+    are not counted;
   * a pending chunk is the next min(s_chunk, remaining) tokens of one
     request's distinct prompt or of one group's prefix; at most one chunk per
     pending item per iteration; the loop stops at the first chunk that does
@@ -95,9 +97,10 @@ def batch_iterations(groups, s_chunk: int, m_threshold: int) -> list:
             break
         batch = []
         memory = 0
+        for g in {g for g, _ in decoding}:
+            memory += 2 * groups[g].prefix_len
         for g, j in decoding:
-            ctx = groups[g].prefix_len + groups[g].distinct[j] + generated[(g, j)]
-            memory += 2 * ctx
+            memory += 2 * (groups[g].distinct[j] + generated[(g, j)])
         for g, j in decoding:
             batch.append((DECODE, g, j, groups[g].prefix_len + groups[g].distinct[j] + generated[(g, j)], 1))
         for kind, g, j, remaining, begin in pending:

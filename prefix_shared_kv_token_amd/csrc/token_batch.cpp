@@ -5,8 +5,8 @@
 // Every iteration takes one decode token from each decoding request, then
 // prefill chunks of at most s_chunk tokens -- distinct prompts of groups whose
 // prefix is done first, then prefixes -- until the next chunk would take the
-// KV memory (2 entries per token; the decoding requests' contexts plus the
-// chunks taken) above the threshold.
+// KV memory (2 entries per token: the decoding groups' prefixes once, the
+// decoding requests' own tokens, the chunks taken) above the threshold.
 //
 // State is kept in queue order so an iteration costs O(entries it emits):
 // the decoding list, the distinct-prompt queue and the prefix queue are
@@ -116,8 +116,12 @@ int rdx_batcher_next(rdx_batcher* b, rdx_tb_entry* out, int32_t cap, int32_t* ou
   // pass 1: how many entries (nothing changes yet)
   const int64_t nd = (int64_t)b->decoding.size();
   int64_t memory = 0;
-  for (int32_t m : b->decoding)
-    memory += 2 * ((int64_t)b->prefix_len[b->group_of[m]] + b->distinct_len[m] + b->generated[m]);
+  // a group's prefix once (decoding is sorted by group), each request's own tokens
+  for (int64_t i = 0; i < nd; ++i) {
+    const int32_t m = b->decoding[i], g = b->group_of[m];
+    if (i == 0 || b->group_of[b->decoding[i - 1]] != g) memory += 2 * (int64_t)b->prefix_len[g];
+    memory += 2 * ((int64_t)b->distinct_len[m] + b->generated[m]);
+  }
   int64_t n_chunks = 0;
   {
     int64_t mem = memory;

@@ -1,0 +1,102 @@
+"""GPU parity of the mixed (token-batched) job: chunked prefill and decode
+tokens of many requests in every attention launch, through the C ABI,
+against the fp64 oracle.  Matched lengths and page-table rows bit-exact;
+outputs within max-abs 1e-4 (fp32) / 2e-2 (bf16).  The small shapes are
+checked on every output; the full BatchLLM-shaped job (the benchmark's
+configuration) on sampled tokens the oracle computes one by one."""
+import numpy as np
+import pytest
+
+from oracle import causal_attention
+from oracle.mixed_run import expected_outputs, run_mixed
+from workloads import Config, Workload, config_by_name, decode_lengths
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+MIX_FP32 = Config("mixed-fp32", 10, 4, 2, 64, "fp32", 1.0, ((6, 40), (3, 20)), 5)
+MIX_BF16 = Config("mixed-bf16", 11, 8, 2, 128, "bf16", 0.5, ((5, 300), (4, 40)), 6)
+
+
+def _run(cfg, s_chunk, m, items=0):
+    import torch
+    from prefix_shared_kv_token_amd.mixed import MixedRun
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wl = Workload(cfg)
+    tlen = decode_lengths(wl)
+    print(f"\n[gpu] mixed {cfg.name} s_chunk={s_chunk} M={m} items={items}", flush=True)
+    run = MixedRun(wl, s_chunk, m, tlen, items=items)
+    run.run(keep_rows=True)
+    torch.cuda.synchronize()
+    return wl, tlen, run
+
+
+def _token_starts(run):
+    return np.concatenate([np.zeros(run.G, np.int64), run.prefix_len[run.member_group].astype(np.int64)])
+
+
+@pytest.mark.parametrize("cfg,s_chunk,m,items", [(MIX_FP32, 64, 262, 0), (MIX_FP32, 7, 14, 0),
+                                                 (MIX_BF16, 256, 948, 0), (MIX_BF16, 64, 400, 48)])
+def test_mixed_small_every_output(cfg, s_chunk, m, items):
+    wl, tlen, run = _run(cfg, s_chunk, m, items)
+    ref = run_mixed(wl, s_chunk, m, tlen)
+    assert run.matched == ref["matched"]
+    assert sorted(run.rows) == sorted(ref["rows"])
+    for rid, row in ref["rows"].items():
+        np.testing.assert_array_equal(run.rows[rid], row)
+    exp = expected_outputs(wl)
+    req, pos = run.job_sources()
+    start = _token_starts(run)
+    o = run.o.float().cpu().numpy()
+    want = np.stack([exp[int(run.req_rid[r])][p - start[r]] for r, p in zip(req, pos)])
+    err = np.abs(o - want).max()
+    print(f"[gpu] {len(req)} tokens in {len(run.iterations)} launches, max abs err {err:.3g}", flush=True)
+    assert err <= TOL[cfg.dtype]
+
+
+def _token_q(wl, r, pos):
+    """Query of request r at position pos (own prompt token or decode token)."""
+    own_start = r.prompt_len - r.own_len
+    if pos < r.prompt_len:
+        return wl.request_q(r)[pos - own_start]
+    return wl.decode_q(r)[pos - r.prompt_len]
+
+
+def test_mixed_batchllm_full_size_sampled():
+    """64 groups x 16 (prefix 2,000, distinct 200, up to 64 generated), chunks
+    of 512, KV memory bound a fifth of the job's -- as the benchmark runs it."""
+    cfg = config_by_name("batchllm")
+    wl = Workload(cfg)
+    tlen = decode_lengths(wl)
+    total = cfg.total_tokens() - (cfg.decode_steps * len(wl.leaf_requests) - int(tlen.sum()))
+    m = 2 * (total // 5)
+    wl, tlen, run = _run(cfg, 512, m)
+    mixed = sum(1 for e in run.iterations if (e[:, 0] == 0).any() and (e[:, 0] != 0).any())
+    assert mixed > 0
+    req, pos = run.job_sources()
+    start = _token_starts(run)
+    rng = np.random.default_rng(17)
+    picks = rng.choice(len(req), 48, replace=False)
+    # also the first and last token of the job and a decode token of a mixed launch
+    picks = np.concatenate([picks, [0, len(req) - 1]])
+    reqs = wl.phases[0].requests + wl.phases[1].requests
+    by_rid = {r.rid: r for r in reqs}
+    worst = 0.0
+    for i in picks:
+        r = by_rid[int(run.req_rid[req[i]])]
+        p = int(pos[i])
+        k, v = wl.request_full_kv(r)
+        want = causal_attention(_token_q(wl, r, p)[None], k, v, np.array([p]))[0]
+        got = run.o[int(i)].float().cpu().numpy()
+        worst = max(worst, float(np.abs(got - want).max()))
+    print(f"[gpu] batchllm mixed: {len(run.iterations)} launches ({mixed} mixed), sampled max abs err {worst:.3g}",
+          flush=True)
+    assert worst <= TOL["bf16"]
+    # indices of sampled requests: each request's row holds its group's
+    # prefix row, then slots no other request holds
+    pre_rows = {int(run.req_rid[g]): run.rows[int(run.req_rid[g])] for g in range(run.G)}
+    assert all(len(row) == run.prefix_len[g] for g, row in enumerate(pre_rows.values()))
+    seen = np.concatenate(list(pre_rows.values()) + [run.rows[int(run.req_rid[run.G + j])][run.prefix_len[g]:]
+                                                     for j, g in enumerate(run.member_group)])
+    assert len(np.unique(seen)) == len(seen) == total

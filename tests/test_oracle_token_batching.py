@@ -40,6 +40,24 @@ def test_worked_example():
     ]
 
 
+def test_shared_prefix_counts_once_in_the_decoding_memory():
+    # one group: prefix 4; members (distinct 1, decode 2) x 2 and (distinct 3,
+    # decode 1); s_chunk 2, M 14
+    groups = [Group(4, (1, 1, 3), (2, 2, 1))]
+    its = batch_iterations(groups, 2, 14)
+    assert its == [
+        [(PREFIX, 0, -1, 0, 2)],
+        [(PREFIX, 0, -1, 2, 2)],
+        # memory 2 + 2 + 4 = 8
+        [(DISTINCT, 0, 0, 4, 1), (DISTINCT, 0, 1, 4, 1), (DISTINCT, 0, 2, 4, 2)],
+        # two decoding requests of the group: prefix once (8) + own tokens
+        # (2 + 2) = 12; the last distinct token fits (14).  Counting the
+        # prefix per request (20) would leave it out.
+        [(DECODE, 0, 0, 5, 1), (DECODE, 0, 1, 5, 1), (DISTINCT, 0, 2, 6, 1)],
+        [(DECODE, 0, 0, 6, 1), (DECODE, 0, 1, 6, 1), (DECODE, 0, 2, 7, 1)],
+    ]
+
+
 def test_unbounded_memory_closed_form():
     """Memory never binds and a chunk holds any prompt: iteration 0 takes
     every prefix, iteration 1 every distinct prompt, then max(decode)
@@ -95,7 +113,8 @@ def _check_run(groups, s_chunk, m, its):
         want = sorted(k for k in own_next if k in prompt_end_it and prompt_end_it[k] < it
                       and gen[k] < groups[k[0]].decode[k[1]])
         assert sorted((g, j) for _, g, j, _, _ in dec) == want
-        mem = sum(2 * (groups[g].prefix_len + groups[g].distinct[j] + gen[(g, j)]) for g, j in want)
+        mem = 2 * sum(groups[g].prefix_len for g in {g for g, _ in want}) + \
+            sum(2 * (groups[g].distinct[j] + gen[(g, j)]) for g, j in want)
         # pending items at the start of the iteration, in queue order
         pending = []
         for g in order:
