@@ -15,7 +15,8 @@ Per iteration (all computation in the library; this module marshals):
   prefix request of a group, or a member once its group's prefix is in the
   tree) -> one slot per decode token (rdx_alloc) -> plan over the mixed
   batch (chunk: kv_len = chunk end, q_len = chunk; decode: q_len = 1) ->
-  upload, KV scatter, extend attention -> finish the requests that completed
+  upload, KV scatter, attention (the extend kernel; the decode kernel when
+  the batch holds decode tokens only) -> finish the requests that completed
   (one rdx_finish: the prefix goes into the tree for the members).
 
 Inputs are staged before the run in the order the tokens are processed
@@ -217,7 +218,12 @@ class MixedRun:
             batch = _Rows(node[req], rows, kv_len, rt._rs.written[rows64])
             n = int(cnt.sum())
             sl = slice(tok, tok + n)
-            rt._launch(rdx.PLAN_EXTEND, batch, cnt, new_slots, self.q[sl], self.k[sl], self.v[sl], self.o[sl])
+            # a batch of decode tokens only runs on the decode kernel (few
+            # query rows per key: bandwidth-bound); any prefill chunk makes it
+            # an extend launch, its decode tokens sharing the tiles of their
+            # group's chunks
+            kind_p = rdx.PLAN_DECODE if n_dec == n_e else rdx.PLAN_EXTEND
+            rt._launch(kind_p, batch, cnt, new_slots, self.q[sl], self.k[sl], self.v[sl], self.o[sl])
             # requests that completed: insert their sequences, unlock, free rows
             fin = kv_len.astype(np.int64) == self.req_total_len[req]
             if fin.any():
