@@ -13,6 +13,8 @@ Passages followed:
   * vLLM-vs-SGLang page, worked example and matching-unit section: the
     reusable length is the match counted from the first token, rounded down
     to the matching unit.
+  * vLLM-vs-SGLang page, eviction passage: besides the default LRU, SGLang
+    offers LFU, SLRU and priority eviction (named only).
 
 This model keeps ONE TRIE NODE PER TOKEN (deliberately not the edge-
 compressed layout of the product's tree).  A radix node ("segment") is a
@@ -37,12 +39,22 @@ Readings of points the pages leave open (the product's tree follows the same):
   * lock/unlock add/subtract 1 on every segment from the node to the root;
     an underflow is a state error and changes nothing;
   * match unit u > 1 truncates the match to a multiple of u before splitting.
+  * eviction policies (the pages name them; these are their textbook forms
+    on the same leaves): every match/insert call that stamps a segment also
+    counts one access to it and raises its priority to the call's priority
+    (set_priority; 0 by default); a new segment starts with one access and
+    the call's priority; a split's upper part copies both.  Victim key, the
+    smallest first: LRU (last access, id); LFU (accesses, last access, id);
+    SLRU (protected = accessed by two or more calls, last access, id) -- the
+    probationary segment is evicted before the protected one; priority
+    (priority, last access, id).
 """
 from __future__ import annotations
 
 import heapq
 
 EINVAL, ENOSPC, ESTATE = -1, -2, -3
+POLICIES = ("lru", "lfu", "slru", "priority")
 _FREE, _TREE, _PRIVATE = 0, 1, 2
 
 
@@ -64,21 +76,25 @@ class _Tok:
 
 
 class _Seg:
-    __slots__ = ("id", "last", "ref", "top")
+    __slots__ = ("id", "last", "ref", "top", "hits", "prio")
 
-    def __init__(self, sid, last, ref, top):
+    def __init__(self, sid, last, ref, top, hits=1, prio=0):
         self.id = sid
         self.last = last
         self.ref = ref
         self.top = top
+        self.hits = hits
+        self.prio = prio
 
 
 class TokenTrieCache:
-    def __init__(self, num_slots: int, match_unit: int = 1):
-        if num_slots <= 0 or match_unit < 1:
-            raise CacheError(EINVAL, "num_slots > 0 and match_unit >= 1 required")
+    def __init__(self, num_slots: int, match_unit: int = 1, policy: str = "lru"):
+        if num_slots <= 0 or match_unit < 1 or policy not in POLICIES:
+            raise CacheError(EINVAL, "num_slots > 0, match_unit >= 1 and a known policy required")
         self.num_slots = num_slots
         self.unit = match_unit
+        self.policy = policy
+        self.priority = 0
         self.root = _Tok(None, -1, 0, None)
         self.segs: dict[int, _Seg] = {}
         self.next_id = 1
@@ -125,7 +141,7 @@ class TokenTrieCache:
         below = self._next_in_seg(tn)
         if below is None:
             return x.id
-        y = _Seg(self.next_id, x.last, x.ref, x.top)
+        y = _Seg(self.next_id, x.last, x.ref, x.top, x.hits, x.prio)
         self.next_id += 1
         n = x.top
         while True:
@@ -140,7 +156,19 @@ class TokenTrieCache:
 
     def _stamp(self, tnodes):
         for sid in {tn.seg for tn in tnodes}:
-            self.segs[sid].last = self.clock
+            sg = self.segs[sid]
+            sg.last = self.clock
+            sg.hits += 1
+            sg.prio = max(sg.prio, self.priority)
+
+    def _victim_key(self, s):
+        if self.policy == "lfu":
+            return (s.hits, s.last, s.id)
+        if self.policy == "slru":
+            return (1 if s.hits >= 2 else 0, s.last, s.id)
+        if self.policy == "priority":
+            return (s.prio, s.last, s.id)
+        return (s.last, s.id)
 
     def _path(self, node_id: int):
         if node_id == 0:
@@ -167,7 +195,7 @@ class TokenTrieCache:
         leaves = [s for s in self.segs.values() if s.ref == 0 and self._is_leaf(s)]
         if not leaves:
             return 0
-        victim = min(leaves, key=lambda s: (s.last, s.id))
+        victim = min(leaves, key=self._victim_key)
         chain = self._chain(victim)
         del victim.top.parent.children[victim.top.tok]
         for tn in chain:
@@ -204,7 +232,7 @@ class TokenTrieCache:
         if k == n:
             self._stamp(nodes)
             return k, (nodes[-1].seg if n else 0)
-        z = _Seg(self.next_id, self.clock, 0, None)
+        z = _Seg(self.next_id, self.clock, 0, None, 1, self.priority)
         self.next_id += 1
         self.segs[z.id] = z
         cur = nodes[-1] if k else self.root
@@ -217,6 +245,10 @@ class TokenTrieCache:
             cur = tn
         self._stamp(nodes)
         return k, z.id
+
+    def set_priority(self, priority: int):
+        """Priority carried by the following match/insert calls."""
+        self.priority = int(priority)
 
     def lock(self, node_id: int):
         for s in self._path(node_id):
@@ -303,7 +335,7 @@ class TokenTrieCache:
             depth += 1
             p = p.parent
         return dict(id=s.id, last=s.last, ref=s.ref, start=depth, length=len(chain),
-                    slots=[tn.slot for tn in chain], leaf=not chain[-1].children)
+                    slots=[tn.slot for tn in chain], leaf=not chain[-1].children, hits=s.hits, prio=s.prio)
 
     def evictable_leaves(self):
         return [s.id for s in self.segs.values() if s.ref == 0 and self._is_leaf(s)]
