@@ -239,12 +239,15 @@ def cpu_baseline(wl, seconds: float):
                       f"BLAS threads = host cores; cpu: {cpu}"}
 
 
-def _serve_in_order(rdx, tree, prompts, order) -> int:
+def _serve_in_order(rdx, tree, prompts, order, priority=None) -> int:
     """Serves the prompts one after another on `tree` (match, lock, allocate
-    the rest, insert, free duplicates, unlock) -> cached prompt tokens."""
+    the rest, insert, free duplicates, unlock) -> cached prompt tokens.
+    priority: per prompt, the priority its calls carry."""
     cached = 0
     for i in order:
         p = prompts[i]
+        if priority is not None:
+            tree.set_priority(int(priority[i]))
         m, slots, node = tree.match_prefix(p)
         if node:
             tree.lock(node)
@@ -294,6 +297,28 @@ def schedule_probe(rdx, window: int = 128, reps: int = 20):
         everything.schedule(prompts)
         ts.append(time.perf_counter() - t0)
     out["schedule_us"] = float(np.median(ts) * 1e6)
+    return out
+
+
+def eviction_probe(rdx, pools=(4000, 6000, 10000)):
+    """Eviction orders (host): a stream of 400 requests, half of them
+    reusing one of four 1,000-token system prompts (popularity 8:4:2:1) plus
+    40 fresh tokens, half one-off 1,500-token prompts, served in arrival
+    order on the C++ tree with each policy; the priority policy gives the
+    reusing requests priority 1.  Hit rate = cached prompt tokens / prompt
+    tokens."""
+    from workloads import reuse_stream
+
+    prompts, hot = reuse_stream()
+    total = sum(len(p) for p in prompts)
+    out = {"stream": "400 requests: 50% one of 4 hot 1000-token prompts (8:4:2:1) + 40, 50% one-off 1500",
+           "prompt_tokens": total}
+    for cap in pools:
+        row = {}
+        for pol in ("lru", "lfu", "slru", "priority"):
+            row[pol] = _serve_in_order(rdx, rdx.Tree(cap, 1, pol), prompts, range(len(prompts)),
+                                       priority=hot.astype(int) if pol == "priority" else None) / total
+        out[f"hit_rate_pool_{cap}"] = row
     return out
 
 
@@ -454,6 +479,7 @@ def main():
     if not args.no_schedule_probe:
         print("[bench] request ordering on the host tree", file=sys.stderr, flush=True)
         line["schedule"] = schedule_probe(rdx)
+        line["eviction"] = eviction_probe(rdx)
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

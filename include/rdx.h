@@ -191,6 +191,24 @@ void rdx_batcher_destroy(rdx_batcher* batcher);
  * (members + groups entries always suffice). */
 int rdx_batcher_next(rdx_batcher* batcher, rdx_tb_entry* out, int32_t cap, int32_t* out_n);
 
+/* Eviction order among unreferenced leaves (vLLM-vs-SGLang page, eviction
+ * passage: SGLang offers LFU, SLRU and priority besides the default LRU;
+ * named only there, taken here in their textbook forms).  Every match or
+ * insert call that stamps a node also counts one access to it and raises
+ * its priority to the call's (rdx_tree_set_priority; 0 by default); a new
+ * node starts with one access and the call's priority; a split's upper part
+ * copies both.  Victim = smallest (major key, last access, node id):
+ * LRU major 0; LFU major = accesses; SLRU major = 1 once accessed by two
+ * calls (protected), else 0 (probation, evicted first); PRIORITY major =
+ * priority.  Errors: EINVAL (unknown policy). */
+#define RDX_EVICT_LRU 0
+#define RDX_EVICT_LFU 1
+#define RDX_EVICT_SLRU 2
+#define RDX_EVICT_PRIORITY 3
+int rdx_tree_set_policy(rdx_tree* tree, int32_t policy);
+/* Priority carried by the tree's following match/insert calls. */
+int rdx_tree_set_priority(rdx_tree* tree, int32_t priority);
+
 typedef struct rdx_stats {
   int64_t num_slots;
   int64_t free;      /* slots in the free set */
@@ -204,7 +222,7 @@ typedef struct rdx_stats {
 int rdx_tree_stats(const rdx_tree* tree, rdx_stats* out);
 
 typedef struct rdx_node_info {
-  int64_t id, parent, start, length, ref, last_access, num_children;
+  int64_t id, parent, start, length, ref, last_access, num_children, hits, priority;
 } rdx_node_info;
 /* Introspection of one node; out_slots (capacity info.length, may be NULL)
  * receives its slots.  Errors: ESTATE (unknown node). */

@@ -156,6 +156,17 @@ int rdx_tree_stats(const rdx_tree* t, rdx_stats* out) {
   return rdx::ok();
 }
 
+int rdx_tree_set_policy(rdx_tree* t, int32_t policy) {
+  if (!t) return fail(RDX_EINVAL, "rdx_tree_set_policy: null tree");
+  return t->impl.set_policy(policy);
+}
+
+int rdx_tree_set_priority(rdx_tree* t, int32_t priority) {
+  if (!t) return fail(RDX_EINVAL, "rdx_tree_set_priority: null tree");
+  t->impl.set_priority(priority);
+  return rdx::ok();
+}
+
 int rdx_node_get(const rdx_tree* t, int64_t node, rdx_node_info* out, int32_t* out_slots) {
   if (!t || !out) return fail(RDX_EINVAL, "rdx_node_get: null argument");
   const rdx::Node* n = t->impl.find(node);
@@ -167,6 +178,8 @@ int rdx_node_get(const rdx_tree* t, int64_t node, rdx_node_info* out, int32_t* o
   out->ref = n->ref;
   out->last_access = n->last_access;
   out->num_children = (int64_t)n->children.size();
+  out->hits = n->hits;
+  out->priority = n->prio;
   if (out_slots)
     for (size_t i = 0; i < n->slots.size(); ++i) out_slots[i] = n->slots[i];
   return rdx::ok();

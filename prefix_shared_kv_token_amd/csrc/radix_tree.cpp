@@ -9,6 +9,12 @@
 //    keeps its id and stamp;
 //  * eviction takes whole unreferenced leaves, smallest (last access, id)
 //    first, and repeats as parents become leaves;
+//  * the other eviction orders (LFU, SLRU, priority; the pages name them
+//    beside LRU): every stamp also counts one access and raises the node's
+//    priority to the call's; a new node starts with one access and the
+//    call's priority; a split's upper part copies both.  The victim is the
+//    smallest (major, last access, id), major = accesses (LFU), protected =
+//    accesses >= 2 (SLRU: probation goes first), priority (priority), 0 (LRU);
 //  * allocation hands out the smallest free slot ids in ascending order and
 //    evicts only the shortfall; it fails without side effects when free +
 //    evictable slots cannot cover the request.
@@ -96,6 +102,8 @@ Node* RadixTree::split(Node* x, int64_t c) {
   y->slots.assign(x->slots.begin(), x->slots.begin() + c);
   y->last_access = x->last_access;
   y->ref = x->ref;
+  y->hits = x->hits;
+  y->prio = x->prio;
   x->key.erase(x->key.begin(), x->key.begin() + c);
   x->slots.erase(x->slots.begin(), x->slots.begin() + c);
   x->start += c;
@@ -116,7 +124,18 @@ Node* RadixTree::node_ending_at(const std::vector<WalkStep>& steps, int64_t d) {
 }
 
 void RadixTree::stamp_to_root(Node* n) {
-  for (Node* p = n; p != nullptr && p != &root_; p = p->parent) p->last_access = clock_;
+  for (Node* p = n; p != nullptr && p != &root_; p = p->parent) {
+    p->last_access = clock_;
+    p->hits++;
+    p->prio = std::max(p->prio, cur_prio_);
+  }
+}
+
+int RadixTree::set_policy(int32_t policy) {
+  if (policy < RDX_EVICT_LRU || policy > RDX_EVICT_PRIORITY)
+    return fail(RDX_EINVAL, "rdx_tree_set_policy: unknown policy %d", policy);
+  policy_ = policy;
+  return ok();
 }
 
 int RadixTree::check_private(const int32_t* slots, int64_t n) {
@@ -181,15 +200,23 @@ int RadixTree::unlock(int64_t id) {
 }
 
 int64_t RadixTree::evict_until(int64_t free_target, int64_t min_freed) {
-  using Key = std::tuple<int64_t, int64_t, Node*>;
+  using Key = std::tuple<int64_t, int64_t, int64_t, Node*>;
   std::priority_queue<Key, std::vector<Key>, std::greater<Key>> leaves;
+  auto major = [this](const Node* x) -> int64_t {
+    switch (policy_) {
+      case RDX_EVICT_LFU: return x->hits;
+      case RDX_EVICT_SLRU: return x->hits >= 2 ? 1 : 0;
+      case RDX_EVICT_PRIORITY: return x->prio;
+      default: return 0;
+    }
+  };
   for (auto& kv : nodes_) {
     Node* x = kv.second.get();
-    if (x->ref == 0 && x->children.empty()) leaves.emplace(x->last_access, x->id, x);
+    if (x->ref == 0 && x->children.empty()) leaves.emplace(major(x), x->last_access, x->id, x);
   }
   int64_t freed = 0;
   while ((num_free() < free_target || freed < min_freed) && !leaves.empty()) {
-    Node* v = std::get<2>(leaves.top());
+    Node* v = std::get<3>(leaves.top());
     leaves.pop();
     Node* parent = v->parent;
     parent->children.erase(v->key[0]);
@@ -201,7 +228,7 @@ int64_t RadixTree::evict_until(int64_t free_target, int64_t min_freed) {
     evictions_++;
     nodes_.erase(v->id);
     if (parent != &root_ && parent->children.empty() && parent->ref == 0)
-      leaves.emplace(parent->last_access, parent->id, parent);
+      leaves.emplace(major(parent), parent->last_access, parent->id, parent);
   }
   return freed;
 }
@@ -269,6 +296,7 @@ int RadixTree::insert(const int32_t* tokens, const int32_t* slots, int64_t n, in
   z->key.assign(tokens + k, tokens + n);
   z->slots.assign(slots + k, slots + n);
   z->last_access = clock_;
+  z->prio = cur_prio_;
   for (int64_t i = k; i < n; ++i) state_[slots[i]] = kTree;
   attach->children[tokens[k]] = z.get();
   stamp_to_root(attach);

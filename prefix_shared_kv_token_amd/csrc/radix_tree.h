@@ -15,6 +15,8 @@
 #include <unordered_map>
 #include <vector>
 
+#include "rdx.h"
+
 namespace rdx {
 
 // Length of the common prefix of a[0..n) and b[0..n): equal 16-token blocks
@@ -36,6 +38,8 @@ struct Node {
   std::unordered_map<int32_t, Node*> children;  // first token -> child
   int64_t last_access = 0;
   int64_t ref = 0;
+  int64_t hits = 1;   // match/insert calls that stamped it (LFU, SLRU)
+  int32_t prio = 0;   // highest priority of those calls (priority eviction)
   int64_t end() const { return start + (int64_t)key.size(); }
   // batch-planner scratch: meaningful only while plan_epoch equals the epoch
   // of the build that is running (builds on one tree are never concurrent)
@@ -61,6 +65,11 @@ class RadixTree {
   int insert(const int32_t* tokens, const int32_t* slots, int64_t n, int64_t* out_present,
              int64_t* out_node);
   int evict(int64_t n_tokens, int64_t* out_freed);
+  // eviction order among unreferenced leaves (RDX_EVICT_*) and the priority
+  // the following match/insert calls carry
+  int set_policy(int32_t policy);
+  void set_priority(int32_t p) { cur_prio_ = p; }
+  int32_t policy() const { return policy_; }
 
   int32_t match_unit() const { return unit_; }
   int64_t num_slots() const { return num_slots_; }
@@ -94,6 +103,8 @@ class RadixTree {
 
   int64_t num_slots_;
   int32_t unit_;
+  int32_t policy_ = RDX_EVICT_LRU;
+  int32_t cur_prio_ = 0;
   Node root_;
   std::unordered_map<int64_t, std::unique_ptr<Node>> nodes_;
   int64_t next_id_ = 1;

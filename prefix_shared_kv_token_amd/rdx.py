@@ -34,7 +34,8 @@ class Stats(ctypes.Structure):
 
 
 class NodeInfo(ctypes.Structure):
-    _fields_ = [(n, i64) for n in ("id", "parent", "start", "length", "ref", "last_access", "num_children")]
+    _fields_ = [(n, i64) for n in ("id", "parent", "start", "length", "ref", "last_access", "num_children",
+                                   "hits", "priority")]
 
 
 class AttnDesc(ctypes.Structure):
@@ -87,6 +88,8 @@ _SIGS = {
     "rdx_batcher_create": (ctypes.c_int, [i32, i32p, i32p, i32p, i32p, i32, i64, ctypes.POINTER(vp)]),
     "rdx_batcher_destroy": (None, [vp]),
     "rdx_batcher_next": (ctypes.c_int, [vp, vp, i32, i32p]),
+    "rdx_tree_set_policy": (ctypes.c_int, [vp, i32]),
+    "rdx_tree_set_priority": (ctypes.c_int, [vp, i32]),
     "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
     "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
     "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),
@@ -160,13 +163,20 @@ def _stream(stream):
 
 
 # --------------------------------------------------------------------- tree
+EVICT_POLICIES = {"lru": 0, "lfu": 1, "slru": 2, "priority": 3}
+
+
 class Tree:
     """rdx_tree: radix tree + slot allocator (host)."""
 
-    def __init__(self, num_slots: int, match_unit: int = 1):
+    def __init__(self, num_slots: int, match_unit: int = 1, policy: str = "lru"):
         h = vp()
         _check(lib().rdx_tree_create(num_slots, match_unit, ctypes.byref(h)))
         self._h = h
+        if policy != "lru":
+            if policy not in EVICT_POLICIES:
+                raise ValueError(f"unknown eviction policy {policy!r}")
+            _check(lib().rdx_tree_set_policy(h, EVICT_POLICIES[policy]))
         self.num_slots = num_slots
         self._buf = np.empty(0, np.int32)
 
@@ -179,6 +189,9 @@ class Tree:
     @property
     def handle(self):
         return self._h
+
+    def set_priority(self, priority: int):
+        _check(lib().rdx_tree_set_priority(self._h, int(priority)))
 
     def match_prefix(self, tokens):
         t = _i32(tokens)

@@ -37,12 +37,16 @@ def _stats_eq(tree, model):
     assert s == o, (s, o)
 
 
-def _run(seed, num_slots, unit, vocab, max_len, steps):
+def _run(seed, num_slots, unit, vocab, max_len, steps, policy="lru"):
     rng = np.random.default_rng(seed)
-    tree, model = rdx.Tree(num_slots, unit), TokenTrieCache(num_slots, unit)
+    tree, model = rdx.Tree(num_slots, unit, policy), TokenTrieCache(num_slots, unit, policy)
     active = []
     for step in range(steps):
         op = rng.random()
+        if policy == "priority" and rng.random() < 0.3:
+            p = int(rng.integers(0, 4))
+            tree.set_priority(p)
+            model.set_priority(p)
         if op < 0.4 or not active:
             seq = list(rng.integers(0, vocab, int(rng.integers(0, max_len))))
             a = _call(tree.match_prefix, seq)
@@ -80,8 +84,9 @@ def _run(seed, num_slots, unit, vocab, max_len, steps):
         else:
             for nid in list(model.segs)[:5]:
                 info, ref = tree.node(nid), model.node_info(nid)
-                assert (info["start"], info["length"], info["ref"], info["last_access"]) == \
-                    (ref["start"], ref["length"], ref["ref"], ref["last"])
+                assert (info["start"], info["length"], info["ref"], info["last_access"], info["hits"],
+                        info["priority"]) == (ref["start"], ref["length"], ref["ref"], ref["last"], ref["hits"],
+                                              ref["prio"])
                 assert list(info["slots"]) == ref["slots"]
         _stats_eq(tree, model)
     return model
@@ -101,3 +106,39 @@ def test_random_ops_unit16(seed):
 @pytest.mark.parametrize("seed", range(5))
 def test_random_ops_large_vocab(seed):
     _run(200 + seed, num_slots=200, unit=1, vocab=50, max_len=30, steps=150)
+
+
+@pytest.mark.parametrize("policy", ["lfu", "slru", "priority"])
+@pytest.mark.parametrize("seed", range(12))
+def test_random_ops_eviction_policies(seed, policy):
+    model = _run(300 + seed, num_slots=30, unit=1 + (seed % 3 == 2), vocab=3, max_len=9, steps=150, policy=policy)
+    assert model.evictions > 0 or seed % 5 == 0
+
+
+def test_reuse_stream_hit_rates_equal_the_oracle():
+    """The measured eviction stream (400 requests, pool of 6,000 slots):
+    the cached prompt tokens under every policy equal the oracle's."""
+    from workloads import reuse_stream
+
+    prompts, hot = reuse_stream()
+
+    def serve(c, prio):
+        cached = 0
+        for p, h in zip(prompts, hot):
+            if prio:
+                c.set_priority(int(h))
+            m, slots, node = c.match_prefix(p)
+            if node:
+                c.lock(node)
+            new = c.alloc(len(p) - m)
+            k, _ = c.insert(p, list(slots) + list(new))
+            if k > m:
+                c.free(list(new)[: k - m])
+            if node:
+                c.unlock(node)
+            cached += m
+        return cached
+
+    for pol in ("lru", "lfu", "slru", "priority"):
+        prio = pol == "priority"
+        assert serve(rdx.Tree(6000, 1, pol), prio) == serve(TokenTrieCache(6000, 1, pol), prio), pol

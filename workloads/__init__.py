@@ -7,9 +7,9 @@ attention); both the HIP path and the oracle consume what it produces.
 """
 from .configs import CONFIGS, Config, config_by_name
 from .gen import Workload, Request, Phase, bf16_round_bits, bf16_bits_to_f32
-from .queue import waiting_queue, decode_lengths
+from .queue import waiting_queue, decode_lengths, reuse_stream
 
 __all__ = [
     "CONFIGS", "Config", "config_by_name", "Workload", "Request", "Phase",
-    "bf16_round_bits", "bf16_bits_to_f32", "waiting_queue", "decode_lengths",
+    "bf16_round_bits", "bf16_bits_to_f32", "waiting_queue", "decode_lengths", "reuse_stream",
 ]

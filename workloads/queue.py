@@ -28,3 +28,30 @@ def decode_lengths(wl: Workload, seed: int = 0) -> np.ndarray:
     t = wl.cfg.decode_steps
     n = len(wl.leaf_requests)
     return rng.integers(1, t + 1, size=n).astype(np.int32) if t > 0 else np.zeros(n, np.int32)
+
+
+def reuse_stream(n: int = 400, seed: int = 0, hot=(1000, 1000, 1000, 1000), weights=(8, 4, 2, 1),
+                 question: int = 40, one_off: int = 1500, p_hot: float = 0.5, vocab: int = 32000):
+    """A request stream that puts a cache under eviction pressure: with
+    probability p_hot a request reuses one of the `hot` system prompts
+    (chosen by `weights`) followed by `question` fresh tokens, else it is a
+    one-off prompt of `one_off` fresh tokens.  -> (prompts, is_hot), in
+    arrival order; hot prompts differ in their first token."""
+    rng = np.random.default_rng(np.random.SeedSequence([SEED, 99, TAG_QUEUE, seed]))
+    firsts = rng.choice(vocab, size=len(hot), replace=False)
+    prefixes = []
+    for f, length in zip(firsts, hot):
+        p = rng.integers(0, vocab, size=length).astype(np.int32)
+        p[0] = f
+        prefixes.append(p)
+    w = np.asarray(weights, np.float64) / np.sum(weights)
+    prompts, is_hot = [], []
+    for _ in range(n):
+        if rng.random() < p_hot:
+            k = int(rng.choice(len(hot), p=w))
+            prompts.append(np.concatenate([prefixes[k], rng.integers(0, vocab, size=question).astype(np.int32)]))
+            is_hot.append(True)
+        else:
+            prompts.append(rng.integers(0, vocab, size=one_off).astype(np.int32))
+            is_hot.append(False)
+    return prompts, np.array(is_hot)
