@@ -300,6 +300,34 @@ def schedule_probe(rdx, window: int = 128, reps: int = 20):
     return out
 
 
+def prefix_groups_probe(rdx, names=("helpdesk", "batchllm", "longprefix", "multilevel"), reps: int = 5):
+    """Global prefix analysis (host): each workload's leaf prompts in a seeded
+    random order grouped by rdx_prefix_groups; R_saving = 1 - N_processed /
+    N_logical with the groups it finds, beside the saving of the radix tree
+    (every shared node computed once, as the attention plans here share
+    every level), and the median time of one call."""
+    import numpy as np
+    from workloads import Workload, config_by_name
+
+    out = {}
+    for name in names:
+        cfg = config_by_name(name)
+        wl = Workload(cfg)
+        leaves = wl.leaf_requests
+        order = np.random.default_rng(cfg.index).permutation(len(leaves))
+        prompts = [wl.prompt_tokens(leaves[i]) for i in order]
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            _, _, ng, proc = rdx.prefix_groups(prompts)
+            ts.append(time.perf_counter() - t0)
+        n_logical = sum(len(p) for p in prompts)
+        distinct = cfg.total_tokens() - cfg.n_leaves * cfg.decode_steps
+        out[name] = {"requests": len(prompts), "groups": ng, "r_saving_groups": 1.0 - proc / n_logical,
+                     "r_saving_radix": 1.0 - distinct / n_logical, "us": float(np.median(ts) * 1e6)}
+    return out
+
+
 def eviction_probe(rdx, pools=(4000, 6000, 10000)):
     """Eviction orders (host): a stream of 400 requests, half of them
     reusing one of four 1,000-token system prompts (popularity 8:4:2:1) plus
@@ -480,6 +508,7 @@ def main():
         print("[bench] request ordering on the host tree", file=sys.stderr, flush=True)
         line["schedule"] = schedule_probe(rdx)
         line["eviction"] = eviction_probe(rdx)
+        line["prefix_groups"] = prefix_groups_probe(rdx)
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -209,6 +209,22 @@ int rdx_tree_set_policy(rdx_tree* tree, int32_t policy);
 /* Priority carried by the tree's following match/insert calls. */
 int rdx_tree_set_priority(rdx_tree* tree, int32_t priority);
 
+/* Global prefix analysis (BatchLLM explainer, Global Prefix Sharing): group
+ * the requests of a batch -- prompt i = tokens[offsets[i] .. offsets[i+1])
+ * -- so that each group's members share the group's prefix (computed once)
+ * and compute the rest of their prompt on their own, choosing the groups by
+ * the dynamic program over the batch's radix tree that minimises
+ *   N_processed = sum of group prefixes + sum of (prompt - group prefix)
+ * (the explainer's gain (leaves(c') - 1) x tokens(c') against the penalty
+ * tokens(c), applied at every node; Equation 2's N_processed).  Ties keep
+ * the higher node: one group for everything below; a request alone below a
+ * branch is grouped at the first token of its own edge.  out_group[i] =
+ * group id (numbered by first request), out_prefix[i] = the group's prefix
+ * length; *out_num_groups, *out_processed = N_processed.  The tree is built
+ * from the sorted prompts, not from the cache.  Errors: EINVAL. */
+int rdx_prefix_groups(int32_t num_reqs, const int32_t* tokens, const int64_t* offsets, int32_t* out_group,
+                      int64_t* out_prefix, int32_t* out_num_groups, int64_t* out_processed);
+
 typedef struct rdx_stats {
   int64_t num_slots;
   int64_t free;      /* slots in the free set */

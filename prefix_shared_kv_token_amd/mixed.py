@@ -10,6 +10,12 @@ decides it; one attention launch then covers the whole batch, the shared
 prefix of a group attended once for all of that group's tokens in it
 (Horizontal Fusion).
 
+At the start of a job the library's global prefix analysis (rdx_prefix_groups,
+BatchLLM explainer, Global Prefix Sharing) groups the members' prompts; the
+groups it finds are the batcher's groups (for the two-level workloads run
+here they are the top-level prefixes, which the staged inputs assume -- a
+different grouping is an error).
+
 Per iteration (all computation in the library; this module marshals):
   rdx_batcher_next -> admit the requests that start (one rdx_admit: the
   prefix request of a group, or a member once its group's prefix is in the
@@ -80,6 +86,7 @@ class MixedRun:
         self.req_prompt_len = np.concatenate([self.prefix_len, self.prefix_len[mg] + self.distinct_len]).astype(np.int64)
         self.req_total_len = self.req_prompt_len + np.concatenate([np.zeros(G, np.int64), self.decode_len])
         prompts = [wl.prompt_tokens(r) for r in pre] + [wl.prompt_tokens(r) for r in mem]
+        self.member_prompts = prompts[G:]
         gen = [np.zeros(0, np.int32)] * G + [wl.decode_tokens(r)[:t] for r, t in zip(mem, self.decode_len)]
         self.seq_tokens = [np.concatenate([p, g]).astype(np.int32) for p, g in zip(prompts, gen)]
         self.rt = Runtime(cfg.dtype, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.total_tokens(), G + M,
@@ -99,7 +106,21 @@ class MixedRun:
         if stage:
             self._stage()
 
-    def _batcher(self):
+    def _batcher(self, analyse: bool = False):
+        """The job's batcher; analyse=True derives its groups from the
+        members' prompts by the global prefix analysis first."""
+        if analyse:
+            group, prefix, ng, _ = rdx.prefix_groups(self.member_prompts)
+            mg = self.member_group
+            # the analysis numbers groups by first member; members come group by group
+            if (ng != self.G or not np.array_equal(group, np.searchsorted(np.unique(mg), mg))
+                    or not np.array_equal(prefix, self.prefix_len[mg])):
+                raise RuntimeError("the prefix analysis grouped the members differently from the workload's "
+                                   "top-level prefixes (the staged inputs assume those)")
+            first = np.searchsorted(group, np.arange(ng))
+            return rdx.Batcher(prefix[first], np.append(first, len(group)).astype(np.int32),
+                               np.array([len(p) for p in self.member_prompts], np.int64) - prefix,
+                               self.decode_len, self.s_chunk, self.m_threshold)
         return rdx.Batcher(self.prefix_len, self.member_offsets, self.distinct_len, self.decode_len,
                            self.s_chunk, self.m_threshold)
 
@@ -171,7 +192,7 @@ class MixedRun:
         matched = np.zeros(n_req, np.int64)
         plen_m = self.prefix_len[self.member_group]
         expect = np.concatenate([np.zeros(G, np.int64), plen_m.astype(np.int64)])
-        b = self._batcher()
+        b = self._batcher(analyse=True)
         p32, p64 = rdx._p32, (lambda x: x.ctypes.data_as(rdx.i64p))
         done_n = rdx.i32()
         tok = 0

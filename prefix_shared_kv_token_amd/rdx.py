@@ -90,6 +90,7 @@ _SIGS = {
     "rdx_batcher_next": (ctypes.c_int, [vp, vp, i32, i32p]),
     "rdx_tree_set_policy": (ctypes.c_int, [vp, i32]),
     "rdx_tree_set_priority": (ctypes.c_int, [vp, i32]),
+    "rdx_prefix_groups": (ctypes.c_int, [i32, i32p, i64p, i32p, i64p, i32p, i64p]),
     "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
     "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
     "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),
@@ -258,6 +259,24 @@ class Tree:
         d = {n: getattr(info, n) for n, _ in NodeInfo._fields_}
         d["slots"] = slots[: info.length].copy()
         return d
+
+
+def prefix_groups(prompts):
+    """Global prefix analysis of a batch -> (group id per request, group
+    prefix length per request, number of groups, N_processed)."""
+    n = len(prompts)
+    offsets = np.zeros(n + 1, np.int64)
+    if n:
+        np.cumsum([len(p) for p in prompts], out=offsets[1:])
+    flat = _i32(np.concatenate([np.asarray(p, np.int32).ravel() for p in prompts]) if n else [])
+    if flat.size == 0:
+        flat = np.zeros(1, np.int32)
+    group = np.empty(max(1, n), np.int32)
+    prefix = np.empty(max(1, n), np.int64)
+    ng, proc = i32(), i64()
+    _check(lib().rdx_prefix_groups(n, _p32(flat), offsets.ctypes.data_as(i64p), _p32(group),
+                                   prefix.ctypes.data_as(i64p), ctypes.byref(ng), ctypes.byref(proc)))
+    return group[:n], prefix[:n], ng.value, proc.value
 
 
 # ------------------------------------------------------------------ batcher
