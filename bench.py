@@ -108,15 +108,16 @@ def run_mixed_bench(args, cfg, wl):
     n_it = len(run.iterations)
     gc.collect()
     gc.freeze()
+    go = run.run if args.mixed_python else run.run_native
     for _ in range(args.warmup):
-        run.run()
+        go()
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} jobs of {n_it} launches", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(args.steps):
         if i == args.steps - 1:
             rdx.timing_begin(n_it)
-        run.run()
+        go()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     attn_ms, merge_ms, _ = rdx.timing_read(n_it)
@@ -162,7 +163,8 @@ def run_mixed_bench(args, cfg, wl):
         "config": {"workload": f"{cfg.name} token-batched", "levels": [list(l) for l in cfg.levels],
                    "max_decode": cfg.decode_steps, "s_chunk": args.s_chunk, "m_threshold": m,
                    "job_tokens": run.n_tokens, "launches": n_it, "mixed_launches": int(mixed.sum()),
-                   "decode_only_launches": int(dec_only.sum()), "parallelism": "none (1 GPU)"},
+                   "decode_only_launches": int(dec_only.sum()), "parallelism": "none (1 GPU)",
+                   "runner": "python" if args.mixed_python else "rdx_job"},
         "roofline": dict(dominant, kernel="extend attention over the mixed batches (all launches)"),
         "roofline_mfma_all": roof_all["mfma"],
         "roofline_hbm_all": roof_all["hbm"],
@@ -366,6 +368,8 @@ def main():
     ap.add_argument("--mixed", action="store_true",
                     help="token-batched job: prefill chunks and decode tokens share each launch")
     ap.add_argument("--s-chunk", type=int, default=512)
+    ap.add_argument("--mixed-python", action="store_true",
+                    help="run the job's iterations from Python (default: rdx_job_* in the library)")
     ap.add_argument("--m-threshold", type=int, default=0,
                     help="KV memory bound in K/V entries (default: a fifth of the job's)")
     ap.add_argument("--extend-items", type=int, default=0)

@@ -417,6 +417,56 @@ int rdx_decode_step(rdx_tree* tree, rdx_plan* plan, const rdx_attn_desc* desc, i
                     int32_t* host_page_table, int64_t num_rows, int64_t ld, int32_t* out_slots,
                     const rdx_step_io* io, void* stream, rdx_plan_info* out_info);
 
+/* A token-batched job run natively (BatchLLM explainer: Throughput-oriented
+ * and Memory-centric Token Batching; Horizontal Fusion): the batcher of the
+ * given groups (arguments as rdx_batcher_create) drives one attention launch
+ * per iteration over `tree`.  Requests: 0..G-1 the groups' prefixes, G + m
+ * member m; request r's full sequence is tokens[offsets[r] .. offsets[r+1])
+ * (offsets[0] = 0): a prefix request holds its prefix, a member its prefix,
+ * distinct prompt and generated tokens (decode_len of them).  The job keeps
+ * its own host page table of num_rows x ld entries (row r of the device
+ * page table mirrors row r).  The group arrays are copied; tokens and
+ * offsets are borrowed and must stay valid until the job is destroyed.
+ * flags:
+ * RDX_JOB_KEEP_ROWS keeps every finished request's row (rdx_job_row);
+ * RDX_JOB_DRY_RUN plans the iterations on the host only (no launch).
+ * Per iteration:
+ *   rdx_job_prepare -- the batcher's entries; admissions in entry order
+ *     (match, lock, allocate the prompt's slots: a prefix request at its
+ *     first chunk, a member at its first distinct chunk); one allocation for
+ *     the decode tokens, in entry order; the plan of the batch (decode_plan
+ *     when it holds decode tokens only, else extend_plan; query tokens in
+ *     entry order, a chunk = positions begin .. begin+count-1 of its
+ *     request).  *out_tokens = the batch's query tokens, 0 once the job is
+ *     done; *out_kind = the plan kind; out_info (may be NULL) its sizes.
+ *   rdx_job_launch -- io->q / k_new / v_new / o hold this iteration's
+ *     tokens in entry order; one kernel stages the plan, writes the page
+ *     table and scatters K/V, then the attention (+ merge).  RDX_ENOBUFS (no
+ *     change, sizes in out_info) if io's plan or workspace buffer is small.
+ *   rdx_job_complete -- the requests whose last token was in the batch are
+ *     inserted (their full sequence, their row's slots), duplicates freed,
+ *     unlocked, rows released; *out_finished = how many.
+ * An error other than ENOBUFS leaves the job unusable (ESTATE afterwards):
+ * destroy it (the tree keeps what was done). */
+#define RDX_JOB_KEEP_ROWS 1
+#define RDX_JOB_DRY_RUN 2
+typedef struct rdx_job rdx_job;
+int rdx_job_create(rdx_tree* tree, int32_t num_groups, const int32_t* prefix_len, const int32_t* member_offsets,
+                   const int32_t* distinct_len, const int32_t* decode_len, int32_t s_chunk, int64_t m_threshold,
+                   const int32_t* tokens, const int64_t* offsets, int32_t num_rows, int64_t ld, int32_t flags,
+                   rdx_job** out);
+void rdx_job_destroy(rdx_job* job);
+int rdx_job_prepare(rdx_job* job, rdx_plan* extend_plan, rdx_plan* decode_plan, int64_t* out_tokens,
+                    int32_t* out_kind, rdx_plan_info* out_info);
+int rdx_job_complete(rdx_job* job, int32_t* out_finished);
+/* A finished request's row (RDX_JOB_KEEP_ROWS): its length, the slots
+ * (capacity cap; ENOBUFS with *out_len if short) and its matched length. */
+int rdx_job_row(const rdx_job* job, int32_t req, int32_t* out, int64_t cap, int64_t* out_len, int64_t* out_matched);
+
+/* The device part of one job iteration (see rdx_job_prepare). */
+int rdx_job_launch(rdx_job* job, const rdx_attn_desc* desc, const rdx_step_io* io, void* stream,
+                   rdx_plan_info* out_info);
+
 /* ------------------------------------------------------- launch timing */
 /* For benchmarks.  rdx_timing_begin(cap) starts recording: the next (up to
  * cap) attention launches are issued with HIP events bound to each kernel

@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librdx.so")
 
-HOST_SOURCES = ["radix_tree.cpp", "plan.cpp", "schedule.cpp", "prefix_groups.cpp", "token_batch.cpp", "capi_host.cpp"]
+HOST_SOURCES = ["radix_tree.cpp", "plan.cpp", "schedule.cpp", "prefix_groups.cpp", "token_batch.cpp", "job.cpp", "capi_host.cpp"]
 HIP_SOURCES = ["device.hip"]
 ARCH = os.environ.get("RDX_OFFLOAD_ARCH", "gfx950")
 # packed fp32 instructions are disabled for all device code

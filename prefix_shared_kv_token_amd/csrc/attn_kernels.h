@@ -1186,6 +1186,15 @@ __global__ void kv_store_kernel(uint4* __restrict__ kp, uint4* __restrict__ vp, 
   }
 }
 
+// Copies a staged work list from mapped pinned host memory to the device
+// plan buffer (16 bytes per thread, grid-stride).  A kernel rather than a
+// DMA copy: queued between kernels on one stream, a host-to-device DMA copy
+// has stalled the stream for milliseconds at a time.
+__global__ void plan_copy_kernel(const int4* __restrict__ src, int4* __restrict__ dst, int64_t n_vec4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec4; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 __global__ void page_table_write_kernel(int32_t* __restrict__ pt, int64_t ld, const int32_t* __restrict__ runs,
                                         const int32_t* __restrict__ run_slots) {
   const int32_t* r = runs + (int64_t)blockIdx.x * kRunWords;

@@ -11,6 +11,7 @@
 
 #include "attn_kernels.h"
 #include "common.h"
+#include "job.h"
 #include "plan.h"
 #include "radix_tree.h"
 
@@ -164,8 +165,9 @@ int stage_done(Plan* p, hipStream_t st) {
   return ok();
 }
 
-// Plan upload: checks, staging through the plan's pinned ring, the H2D copy
-// and (write_pt) the page-table write kernel.
+// Plan upload: checks, staging through the plan's pinned ring, the copy to
+// the device (a kernel reading the mapped staging buffer) and (write_pt) the
+// page-table write kernel.
 // zero_copy: stage only (no copy, no page-table kernel, no event): the
 // caller launches a kernel that reads the staging buffer through
 // *out_stage_dev and then calls stage_done() behind it.
@@ -191,15 +193,22 @@ int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_t
     sg.pending = false;
   }
   if (sg.bytes < bytes) {
-    if (sg.pinned) hipHostFree(sg.pinned);
-    sg.pinned = nullptr;
-    sg.bytes = 0;
+    // every stage of the ring grows at once (pinning memory is slow: one
+    // stall per new size, not one per stage), and outgrown buffers are freed
+    // with the plan (freeing pinned memory waits for the device; a buffer
+    // still read by a queued copy stays valid)
     const int64_t want = bytes + bytes / 2 + 4096;
-    e = hipHostMalloc(&sg.pinned, want, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
-    sg.bytes = want;
-    e = hipHostGetDevicePointer(&sg.pinned_dev, sg.pinned, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipHostGetDevicePointer");
+    for (Plan::Stage& o : p->stages) {
+      if (o.bytes >= want) continue;
+      if (o.pinned) p->retired.push_back(o.pinned);
+      o.pinned = nullptr;
+      o.bytes = 0;
+      e = hipHostMalloc(&o.pinned, want, hipHostMallocDefault);
+      if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+      o.bytes = want;
+      e = hipHostGetDevicePointer(&o.pinned_dev, o.pinned, 0);
+      if (e != hipSuccess) return hip_fail(e, "hipHostGetDevicePointer");
+    }
   }
   int32_t* h = reinterpret_cast<int32_t*>(sg.pinned);
   auto put = [&](int64_t off, const std::vector<int32_t>& v) {
@@ -220,8 +229,13 @@ int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_t
     *out_stage_dev = reinterpret_cast<const int32_t*>(sg.pinned_dev);
     return ok();
   }
-  e = hipMemcpyAsync(dev_plan, sg.pinned, bytes, hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
+  const int64_t n_vec4 = (p->total_words + 3) / 4;  // total_words is a multiple of 16
+  int64_t n_copy = (n_vec4 + 255) / 256;
+  if (n_copy > 512) n_copy = 512;
+  hipLaunchKernelGGL(plan_copy_kernel, dim3((unsigned)n_copy), dim3(256), 0, st,
+                     reinterpret_cast<const int4*>(sg.pinned_dev), reinterpret_cast<int4*>(dev_plan), n_vec4);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "plan copy launch");
   if (write_pt && n_runs > 0) {
     const int32_t* db = reinterpret_cast<const int32_t*>(dev_plan);
     hipLaunchKernelGGL(page_table_write_kernel, dim3((unsigned)n_runs), dim3(256), 0, st, page_table, p->ld,
@@ -273,6 +287,7 @@ void rdx_plan_destroy(rdx_plan* hplan) {
     if (sg.event) hipEventDestroy(reinterpret_cast<hipEvent_t>(sg.event));
     if (sg.pinned) hipHostFree(sg.pinned);
   }
+  for (void* r : p->retired) hipHostFree(r);
   delete p;
 }
 
@@ -288,6 +303,91 @@ int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const 
                          int64_t workspace_bytes, void* stream) {
   return launch_attention(desc, plan, RDX_PLAN_DECODE, dev_plan, q, k_pool, v_pool, page_table, o, workspace,
                           workspace_bytes, stream);
+}
+
+// The device tail of a step whose plan is built: the work list staged in
+// mapped pinned memory, ONE kernel that copies it to the device plan buffer,
+// writes the page-table entries and scatters the num_new new K/V rows into
+// their slots, then the attention (+ merge) launch of `kind`.
+static int store_and_attend(Plan* p, rdx_plan* hplan, const rdx_attn_desc* desc, int32_t kind, const rdx_step_io* io,
+                            void* stream, int64_t ld, int64_t num_new) {
+  const int64_t esize = desc->dtype == RDX_BF16 ? 2 : 4;
+  const int64_t row_bytes = (int64_t)desc->num_kv_heads * desc->head_dim * esize;
+  if (row_bytes % 16) return fail(RDX_EUNSUPPORTED, "step: KV row of %lld bytes", (long long)row_bytes);
+  if (!io->dev_plan || !io->page_table || !io->k_pool || !io->v_pool || !io->q || !io->k_new || !io->v_new || !io->o)
+    return fail(RDX_EINVAL, "step: null device pointer");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
+  const int64_t row_vecs = row_bytes / 16, total = num_new * row_vecs;
+  // The fused kernel reads the staged list through PCIe: right for a decode
+  // step (a few KB, one page-table entry per run).  A batch that admits
+  // requests writes whole rows and carries a large list: copy it by DMA,
+  // then write the page table and scatter K/V from device memory.
+  if ((int64_t)p->run_slots.size() > n_runs + 256 || p->total_words > (int64_t)1 << 18) {
+    int rc = upload_plan(p, io->dev_plan, io->dev_plan_bytes, io->page_table, io->page_table_rows, st, true);
+    if (rc) return rc;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (total > 0) {
+      hipLaunchKernelGGL(kv_store_kernel, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint4*>(io->k_pool),
+                         reinterpret_cast<uint4*>(io->v_pool), reinterpret_cast<const uint4*>(io->k_new),
+                         reinterpret_cast<const uint4*>(io->v_new),
+                         reinterpret_cast<const int32_t*>(io->dev_plan) + p->off_new, num_new, row_vecs);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "KV store launch");
+    }
+    return launch_attention(desc, hplan, kind, io->dev_plan, io->q, io->k_pool, io->v_pool, io->page_table, io->o,
+                            io->workspace, io->workspace_bytes, stream);
+  }
+  const int32_t* hs = nullptr;  // the staged work list, device-addressable
+  int rc = upload_plan(p, io->dev_plan, io->dev_plan_bytes, io->page_table, io->page_table_rows, st, false, true, &hs);
+  if (rc) return rc;
+  const int64_t n_vec4 = (p->total_words + 3) / 4;  // total_words is a multiple of 16
+  int64_t n_copy = (n_vec4 + 255) / 256;
+  if (n_copy > 64) n_copy = 64;
+  int64_t kv_blocks = (total + 255) / 256;
+  if (kv_blocks > 65536) kv_blocks = 65536;
+  const int64_t n_pt = (n_runs + 255) / 256;
+  hipLaunchKernelGGL(step_store_kernel, dim3((unsigned)(n_copy + n_pt + kv_blocks)), dim3(256), 0, st,
+                     reinterpret_cast<const int4*>(hs), reinterpret_cast<int4*>(io->dev_plan), n_vec4,
+                     (int32_t)n_copy, io->page_table, ld, hs + p->off_runs, hs + p->off_run_slots, (int32_t)n_runs,
+                     reinterpret_cast<uint4*>(io->k_pool), reinterpret_cast<uint4*>(io->v_pool),
+                     reinterpret_cast<const uint4*>(io->k_new), reinterpret_cast<const uint4*>(io->v_new),
+                     hs + p->off_new, num_new, row_vecs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "step store launch");
+  rc = stage_done(p, st);
+  if (rc) return rc;
+  return launch_attention(desc, hplan, kind, io->dev_plan, io->q, io->k_pool, io->v_pool, io->page_table, io->o,
+                          io->workspace, io->workspace_bytes, stream);
+}
+
+int rdx_job_launch(rdx_job* j, const rdx_attn_desc* desc, const rdx_step_io* io, void* stream,
+                   rdx_plan_info* out_info) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!j || !io) return fail(RDX_EINVAL, "rdx_job_launch: bad arguments");
+  if (j->broken) return fail(RDX_ESTATE, "rdx_job_launch: an earlier error left the job inconsistent");
+  if (j->state != 1) return fail(RDX_ESTATE, "rdx_job_launch: no prepared iteration");
+  if (j->dry_run) return fail(RDX_ESTATE, "rdx_job_launch: a dry-run job launches nothing");
+  Plan* p = j->plan;
+  if (!same_shape(*desc, p->desc)) return fail(RDX_EINVAL, "rdx_job_launch: descriptor differs from the plan's");
+  rdx_plan_info info;
+  p->fill_info(&info);
+  if (out_info) *out_info = info;
+  if (io->dev_plan_bytes < info.device_bytes || (info.workspace_bytes > 0 && io->workspace_bytes < info.workspace_bytes))
+    return fail(RDX_ENOBUFS, "rdx_job_launch: buffers of %lld (plan) and %lld (workspace) bytes needed",
+                (long long)info.device_bytes, (long long)info.workspace_bytes);
+  if (io->page_table_rows < j->num_rows)
+    return fail(RDX_EINVAL, "rdx_job_launch: device page table has %lld rows, the job uses %d",
+                (long long)io->page_table_rows, j->num_rows);
+  rc = store_and_attend(p, reinterpret_cast<rdx_plan*>(p), desc, j->kind, io, stream, j->ld, j->n_tokens);
+  if (rc) {
+    j->broken = true;
+    return rc;
+  }
+  j->state = 2;
+  return ok();
 }
 
 int rdx_decode_step(rdx_tree* tree, rdx_plan* hplan, const rdx_attn_desc* desc, int32_t num_reqs,
@@ -340,34 +440,8 @@ int rdx_decode_step(rdx_tree* tree, rdx_plan* hplan, const rdx_attn_desc* desc, 
   if (num_reqs > 0 && (!io->dev_plan || !io->page_table || !io->k_pool || !io->v_pool || !io->q || !io->k_new ||
                        !io->v_new || !io->o))
     return undo(fail(RDX_EINVAL, "rdx_decode_step: null device pointer"));
-  const int64_t esize = desc->dtype == RDX_BF16 ? 2 : 4;
-  const int64_t row_bytes = (int64_t)desc->num_kv_heads * desc->head_dim * esize;
-  if (row_bytes % 16) return undo(fail(RDX_EUNSUPPORTED, "rdx_decode_step: KV row of %lld bytes", (long long)row_bytes));
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (num_reqs > 0) {
-    const int32_t* hs = nullptr;  // the staged work list, device-addressable
-    rc = upload_plan(p, io->dev_plan, io->dev_plan_bytes, io->page_table, io->page_table_rows, st, false, true, &hs);
-    if (rc) return undo(rc);
-    const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
-    const int64_t row_vecs = row_bytes / 16, total = (int64_t)num_reqs * row_vecs;
-    const int64_t n_vec4 = (p->total_words + 3) / 4;  // total_words is a multiple of 16
-    int64_t n_copy = (n_vec4 + 255) / 256;
-    if (n_copy > 64) n_copy = 64;
-    int64_t kv_blocks = (total + 255) / 256;
-    if (kv_blocks > 65536) kv_blocks = 65536;
-    const int64_t n_pt = (n_runs + 255) / 256;
-    hipLaunchKernelGGL(step_store_kernel, dim3((unsigned)(n_copy + n_pt + kv_blocks)), dim3(256), 0, st,
-                       reinterpret_cast<const int4*>(hs), reinterpret_cast<int4*>(io->dev_plan), n_vec4,
-                       (int32_t)n_copy, io->page_table, ld, hs + p->off_runs, hs + p->off_run_slots, (int32_t)n_runs,
-                       reinterpret_cast<uint4*>(io->k_pool), reinterpret_cast<uint4*>(io->v_pool),
-                       reinterpret_cast<const uint4*>(io->k_new), reinterpret_cast<const uint4*>(io->v_new),
-                       hs + p->off_new, (int64_t)num_reqs, row_vecs);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return undo(hip_fail(e, "step store launch"));
-    rc = stage_done(p, st);
-    if (rc) return undo(rc);
-    rc = launch_attention(desc, hplan, RDX_PLAN_DECODE, io->dev_plan, io->q, io->k_pool, io->v_pool, io->page_table,
-                          io->o, io->workspace, io->workspace_bytes, stream);
+    rc = store_and_attend(p, hplan, desc, RDX_PLAN_DECODE, io, stream, ld, num_reqs);
     if (rc) return undo(rc);
   }
   // commit: the new slots into the host page-table rows, lengths, written counts

@@ -70,6 +70,7 @@ struct Plan {
     bool pending = false;
   } stages[kStages];
   int64_t uploads = 0;
+  std::vector<void*> retired;  // outgrown staging buffers, freed with the plan
 
   // query rows per tile: 256 for the wide bf16 head_dim-128 extend kernel,
   // kDecodeTileRows for the bf16 decode kernel, kTileRows otherwise

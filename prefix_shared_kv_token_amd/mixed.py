@@ -87,6 +87,9 @@ class MixedRun:
         self.req_total_len = self.req_prompt_len + np.concatenate([np.zeros(G, np.int64), self.decode_len])
         prompts = [wl.prompt_tokens(r) for r in pre] + [wl.prompt_tokens(r) for r in mem]
         self.member_prompts = prompts[G:]
+        # the same prompts as one flat token buffer, as a serving loop holds them
+        self._mp_flat = np.concatenate(self.member_prompts).astype(np.int32) if M else np.zeros(0, np.int32)
+        self._mp_off = np.concatenate([[0], np.cumsum([len(p) for p in self.member_prompts])]).astype(np.int64)
         gen = [np.zeros(0, np.int32)] * G + [wl.decode_tokens(r)[:t] for r, t in zip(mem, self.decode_len)]
         self.seq_tokens = [np.concatenate([p, g]).astype(np.int32) for p, g in zip(prompts, gen)]
         self.rt = Runtime(cfg.dtype, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.total_tokens(), G + M,
@@ -106,23 +109,81 @@ class MixedRun:
         if stage:
             self._stage()
 
+    def _analysed_groups(self):
+        """The batcher's groups from the global prefix analysis of the
+        members' prompts: (prefix per group, member offsets, distinct per
+        member)."""
+        group, prefix, ng, _ = rdx.prefix_groups_flat(self._mp_flat, self._mp_off)
+        mg = self.member_group
+        # the analysis numbers groups by first member; members come group by group
+        if (ng != self.G or not np.array_equal(group, np.searchsorted(np.unique(mg), mg))
+                or not np.array_equal(prefix, self.prefix_len[mg])):
+            raise RuntimeError("the prefix analysis grouped the members differently from the workload's "
+                               "top-level prefixes (the staged inputs assume those)")
+        first = np.searchsorted(group, np.arange(ng))
+        return (prefix[first], np.append(first, len(group)).astype(np.int32), np.diff(self._mp_off) - prefix)
+
     def _batcher(self, analyse: bool = False):
         """The job's batcher; analyse=True derives its groups from the
         members' prompts by the global prefix analysis first."""
         if analyse:
-            group, prefix, ng, _ = rdx.prefix_groups(self.member_prompts)
-            mg = self.member_group
-            # the analysis numbers groups by first member; members come group by group
-            if (ng != self.G or not np.array_equal(group, np.searchsorted(np.unique(mg), mg))
-                    or not np.array_equal(prefix, self.prefix_len[mg])):
-                raise RuntimeError("the prefix analysis grouped the members differently from the workload's "
-                                   "top-level prefixes (the staged inputs assume those)")
-            first = np.searchsorted(group, np.arange(ng))
-            return rdx.Batcher(prefix[first], np.append(first, len(group)).astype(np.int32),
-                               np.array([len(p) for p in self.member_prompts], np.int64) - prefix,
-                               self.decode_len, self.s_chunk, self.m_threshold)
+            return rdx.Batcher(*self._analysed_groups(), self.decode_len, self.s_chunk, self.m_threshold)
         return rdx.Batcher(self.prefix_len, self.member_offsets, self.distinct_len, self.decode_len,
                            self.s_chunk, self.m_threshold)
+
+    def run_native(self, keep_rows: bool = False, dry_run: bool = False):
+        """The job through rdx_job_* (admissions, decode slots, plans and
+        finishes in the library; three calls per iteration)."""
+        rt = self.rt
+        rt.reset()
+        self.matched, self.rows = {}, {}
+        prefix, offs, distinct = self._analysed_groups()
+        if not hasattr(self, "_seq_flat"):
+            # every request's full sequence as one flat buffer (borrowed by the job)
+            self._seq_flat = np.concatenate(self.seq_tokens).astype(np.int32)
+            self._seq_off = np.concatenate([[0], np.cumsum([len(t) for t in self.seq_tokens])]).astype(np.int64)
+        flags = (rdx.JOB_KEEP_ROWS if keep_rows else 0) | (rdx.JOB_DRY_RUN if dry_run else 0)
+        job = rdx.Job(rt.tree, prefix, offs, distinct, self.decode_len, self.s_chunk, self.m_threshold,
+                      self._seq_flat, self._seq_off, rt.max_rows, rt.ld, flags)
+        L = rdx.lib()
+        io = rt._io
+        io_ref = rt._io_ref
+        info = job.info
+        plans = rt.plans
+        ext, dec = plans[rdx.PLAN_EXTEND], plans[rdx.PLAN_DECODE]
+        st = None if dry_run else self.torch.cuda.current_stream().cuda_stream
+        q0 = k0 = v0 = o0 = 0
+        if not dry_run:
+            q0, k0, v0, o0 = self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr()
+            qrow = self.q[0].numel() * self.q.element_size()
+            krow = self.k[0].numel() * self.k.element_size()
+        tok = 0
+        it = 0
+        while True:
+            n, kind = job.prepare(ext, dec)
+            if n == 0:
+                break
+            if not dry_run:
+                dp = rt._dev_plan(kind, info.device_bytes)
+                ws = rt._workspace(info.workspace_bytes)
+                io.dev_plan, io.dev_plan_bytes = dp.data_ptr(), dp.numel()
+                io.workspace, io.workspace_bytes = ws.data_ptr(), ws.numel()
+                io.q, io.o = q0 + tok * qrow, o0 + tok * qrow
+                io.k_new, io.v_new = k0 + tok * krow, v0 + tok * krow
+                rdx._check(L.rdx_job_launch(job.handle, rt._desc_ref, io_ref, st, None))
+            job.complete()
+            tok += n
+            it += 1
+        if tok != self.n_tokens or it != len(self.iterations):
+            raise RuntimeError("the batcher's run differs from the staged one")
+        if keep_rows:
+            for r in range(self.G + self.M):
+                if self.req_total_len[r] == 0:
+                    continue
+                row, m = job.row(r)
+                rid = int(self.req_rid[r])
+                self.rows[rid], self.matched[rid] = row, m
+        return None if dry_run else self.o
 
     # ------------------------------------------------------------ inputs
     def job_sources(self):

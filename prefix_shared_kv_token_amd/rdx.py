@@ -91,6 +91,13 @@ _SIGS = {
     "rdx_tree_set_policy": (ctypes.c_int, [vp, i32]),
     "rdx_tree_set_priority": (ctypes.c_int, [vp, i32]),
     "rdx_prefix_groups": (ctypes.c_int, [i32, i32p, i64p, i32p, i64p, i32p, i64p]),
+    "rdx_job_create": (ctypes.c_int, [vp, i32, i32p, i32p, i32p, i32p, i32, i64, i32p, i64p, i32, i64, i32,
+                                       ctypes.POINTER(vp)]),
+    "rdx_job_destroy": (None, [vp]),
+    "rdx_job_prepare": (ctypes.c_int, [vp, vp, vp, i64p, i32p, vp]),
+    "rdx_job_launch": (ctypes.c_int, [vp, vp, vp, vp, vp]),
+    "rdx_job_complete": (ctypes.c_int, [vp, i32p]),
+    "rdx_job_row": (ctypes.c_int, [vp, i32, i32p, i64, i64p, i64p]),
     "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
     "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
     "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),
@@ -269,6 +276,14 @@ def prefix_groups(prompts):
     if n:
         np.cumsum([len(p) for p in prompts], out=offsets[1:])
     flat = _i32(np.concatenate([np.asarray(p, np.int32).ravel() for p in prompts]) if n else [])
+    return prefix_groups_flat(flat, offsets)
+
+
+def prefix_groups_flat(flat, offsets):
+    """prefix_groups of the prompts flat[offsets[i]:offsets[i+1]]."""
+    flat = _i32(flat)
+    offsets = np.ascontiguousarray(offsets, np.int64)
+    n = len(offsets) - 1
     if flat.size == 0:
         flat = np.zeros(1, np.int32)
     group = np.empty(max(1, n), np.int32)
@@ -310,6 +325,62 @@ class Batcher:
         internal buffer, valid until the next call."""
         _check(lib().rdx_batcher_next(self._h, self._buf.ctypes.data, self._cap, ctypes.byref(self._n)))
         return self._buf[: self._n.value]
+
+
+# ---------------------------------------------------------------------- job
+JOB_KEEP_ROWS, JOB_DRY_RUN = 1, 2
+
+
+class Job:
+    """rdx_job: a token-batched job run natively over a tree, one iteration
+    per prepare / launch / complete."""
+
+    def __init__(self, tree: "Tree", prefix_len, member_offsets, distinct_len, decode_len, s_chunk: int,
+                 m_threshold: int, seq_tokens, seq_offsets, num_rows: int, ld: int, flags: int = 0):
+        arrs = [_i32(prefix_len), _i32(member_offsets), _i32(distinct_len), _i32(decode_len)]
+        toks = _i32(seq_tokens) if len(seq_tokens) else np.zeros(1, np.int32)
+        offs = np.ascontiguousarray(seq_offsets, np.int64)
+        h = vp()
+        _check(lib().rdx_job_create(tree.handle, len(arrs[0]), *[_p32(a) for a in arrs], s_chunk, m_threshold,
+                                    _p32(toks), offs.ctypes.data_as(i64p), num_rows, ld, flags, ctypes.byref(h)))
+        self._h = h
+        self.tree = tree  # the job borrows the tree and the sequences
+        self._keep = (toks, offs)
+        self.info = PlanInfo()
+        self._n, self._kind, self._fin = i64(), i32(), i32()
+        self._refs = (ctypes.byref(self._n), ctypes.byref(self._kind), ctypes.byref(self.info),
+                      ctypes.byref(self._fin))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.rdx_job_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def prepare(self, extend_plan: "Plan", decode_plan: "Plan"):
+        """-> (query tokens of the next iteration (0: done), plan kind)."""
+        _check(lib().rdx_job_prepare(self._h, extend_plan.handle, decode_plan.handle, self._refs[0], self._refs[1],
+                                     self._refs[2]))
+        return self._n.value, self._kind.value
+
+    def complete(self) -> int:
+        _check(lib().rdx_job_complete(self._h, self._refs[3]))
+        return self._fin.value
+
+    def row(self, req: int):
+        """-> (final page-table row, matched length) of a finished request."""
+        n, m = i64(), i64()
+        buf = np.empty(1, np.int32)
+        rc = lib().rdx_job_row(self._h, req, _p32(buf), 0, ctypes.byref(n), ctypes.byref(m))
+        if rc not in (OK, ENOBUFS):
+            _check(rc)
+        buf = np.empty(max(1, n.value), np.int32)
+        _check(lib().rdx_job_row(self._h, req, _p32(buf), len(buf), ctypes.byref(n), ctypes.byref(m)))
+        return buf[: n.value], m.value
 
 
 # --------------------------------------------------------------------- plan

@@ -18,16 +18,19 @@ MIX_FP32 = Config("mixed-fp32", 10, 4, 2, 64, "fp32", 1.0, ((6, 40), (3, 20)), 5
 MIX_BF16 = Config("mixed-bf16", 11, 8, 2, 128, "bf16", 0.5, ((5, 300), (4, 40)), 6)
 
 
-def _run(cfg, s_chunk, m, items=0):
+def _run(cfg, s_chunk, m, items=0, native=True):
     import torch
     from prefix_shared_kv_token_amd.mixed import MixedRun
 
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     wl = Workload(cfg)
     tlen = decode_lengths(wl)
-    print(f"\n[gpu] mixed {cfg.name} s_chunk={s_chunk} M={m} items={items}", flush=True)
+    print(f"\n[gpu] mixed {cfg.name} s_chunk={s_chunk} M={m} items={items} native={native}", flush=True)
     run = MixedRun(wl, s_chunk, m, tlen, items=items)
-    run.run(keep_rows=True)
+    if native:
+        run.run_native(keep_rows=True)
+    else:
+        run.run(keep_rows=True)
     torch.cuda.synchronize()
     return wl, tlen, run
 
@@ -36,10 +39,11 @@ def _token_starts(run):
     return np.concatenate([np.zeros(run.G, np.int64), run.prefix_len[run.member_group].astype(np.int64)])
 
 
+@pytest.mark.parametrize("native", [True, False], ids=["rdx_job", "python"])
 @pytest.mark.parametrize("cfg,s_chunk,m,items", [(MIX_FP32, 64, 262, 0), (MIX_FP32, 7, 14, 0),
                                                  (MIX_BF16, 256, 948, 0), (MIX_BF16, 64, 400, 48)])
-def test_mixed_small_every_output(cfg, s_chunk, m, items):
-    wl, tlen, run = _run(cfg, s_chunk, m, items)
+def test_mixed_small_every_output(cfg, s_chunk, m, items, native):
+    wl, tlen, run = _run(cfg, s_chunk, m, items, native)
     ref = run_mixed(wl, s_chunk, m, tlen)
     assert run.matched == ref["matched"]
     assert sorted(run.rows) == sorted(ref["rows"])

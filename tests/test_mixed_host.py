@@ -94,3 +94,36 @@ def test_runner_host_path_matches_the_oracle(cfg, s_chunk, m, monkeypatch):
     assert sorted(run.rows) == sorted(ref["rows"])
     for rid, row in ref["rows"].items():
         np.testing.assert_array_equal(run.rows[rid], row)
+
+
+@pytest.mark.parametrize("cfg,s_chunk,m", [(MIX_FP32, 64, 262), (MIX_FP32, 7, 14), (MIX_BF16, 256, 948)])
+def test_native_job_dry_run_matches_the_oracle(cfg, s_chunk, m):
+    """rdx_job_* planning the whole job on the host (no launch): every plan
+    builds and every request's matched length and row equal the oracle's."""
+    from prefix_shared_kv_token_amd.mixed import MixedRun
+
+    wl = Workload(cfg)
+    tlen = decode_lengths(wl)
+    run = MixedRun(wl, s_chunk, m, tlen, device="cpu", stage=False)
+    run.run_native(keep_rows=True, dry_run=True)
+    ref = run_mixed(wl, s_chunk, m, tlen)
+    assert run.matched == ref["matched"]
+    assert sorted(run.rows) == sorted(ref["rows"])
+    for rid, row in ref["rows"].items():
+        np.testing.assert_array_equal(run.rows[rid], row)
+    # the tree ends holding every request's sequence, nothing locked
+    st = run.rt.tree.stats()
+    assert st["private"] == 0 and st["evictable"] == st["cached"]
+
+
+def test_native_job_errors():
+    from prefix_shared_kv_token_amd import rdx
+
+    tree = rdx.Tree(64)
+    # member sequence length inconsistent with prefix + distinct + decode
+    with pytest.raises(rdx.RdxError):
+        rdx.Job(tree, [2], [0, 1], [2], [1], 4, 8, [1, 2, 1, 2, 3, 4], [0, 2, 6], 4, 16)
+    job = rdx.Job(tree, [2], [0, 1], [2], [1], 4, 8, [1, 2, 1, 2, 3, 4, 5], [0, 2, 7], 4, 16, rdx.JOB_DRY_RUN)
+    # complete before prepare is a state error
+    with pytest.raises(rdx.RdxError):
+        job.complete()
