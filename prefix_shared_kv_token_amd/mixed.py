@@ -54,9 +54,11 @@ class _Rows:
 
 class MixedRun:
     def __init__(self, wl, s_chunk: int, m_threshold: int, decode_len=None, device="cuda", items: int = 0,
-                 stage: bool = True):
+                 stage: bool = True, num_slots: int | None = None):
         """decode_len: tokens each member generates (<= the workload's
-        decode_steps; all of them by default)."""
+        decode_steps; all of them by default).  num_slots: KV pool size (the
+        workload's distinct tokens by default; a smaller pool makes admissions
+        evict finished requests' tokens)."""
         import torch
 
         self.torch = torch
@@ -92,7 +94,7 @@ class MixedRun:
         self._mp_off = np.concatenate([[0], np.cumsum([len(p) for p in self.member_prompts])]).astype(np.int64)
         gen = [np.zeros(0, np.int32)] * G + [wl.decode_tokens(r)[:t] for r, t in zip(mem, self.decode_len)]
         self.seq_tokens = [np.concatenate([p, g]).astype(np.int32) for p, g in zip(prompts, gen)]
-        self.rt = Runtime(cfg.dtype, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.total_tokens(), G + M,
+        self.rt = Runtime(cfg.dtype, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, num_slots or cfg.total_tokens(), G + M,
                           cfg.max_seq_len, device, extend_items=items)
         # the job's iterations (the batcher is deterministic: the timed run
         # asks it again and gets the same entries)

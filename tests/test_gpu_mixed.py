@@ -18,7 +18,7 @@ MIX_FP32 = Config("mixed-fp32", 10, 4, 2, 64, "fp32", 1.0, ((6, 40), (3, 20)), 5
 MIX_BF16 = Config("mixed-bf16", 11, 8, 2, 128, "bf16", 0.5, ((5, 300), (4, 40)), 6)
 
 
-def _run(cfg, s_chunk, m, items=0, native=True):
+def _run(cfg, s_chunk, m, items=0, native=True, num_slots=None):
     import torch
     from prefix_shared_kv_token_amd.mixed import MixedRun
 
@@ -26,7 +26,7 @@ def _run(cfg, s_chunk, m, items=0, native=True):
     wl = Workload(cfg)
     tlen = decode_lengths(wl)
     print(f"\n[gpu] mixed {cfg.name} s_chunk={s_chunk} M={m} items={items} native={native}", flush=True)
-    run = MixedRun(wl, s_chunk, m, tlen, items=items)
+    run = MixedRun(wl, s_chunk, m, tlen, items=items, num_slots=num_slots)
     if native:
         run.run_native(keep_rows=True)
     else:
@@ -57,6 +57,26 @@ def test_mixed_small_every_output(cfg, s_chunk, m, items, native):
     err = np.abs(o - want).max()
     print(f"[gpu] {len(req)} tokens in {len(run.iterations)} launches, max abs err {err:.3g}", flush=True)
     assert err <= TOL[cfg.dtype]
+
+
+def test_mixed_under_eviction_every_output():
+    """A pool of 300 slots for a job of 660 tokens: admissions evict finished
+    requests (the slots of their pages are reused while later launches read
+    their own); rows bit-exact, every output within tolerance."""
+    wl, tlen, run = _run(MIX_FP32, 64, 262, num_slots=300)
+    ref = run_mixed(wl, 64, 262, tlen, num_slots=300)
+    assert ref["stats"]["evictions"] > 0
+    assert run.matched == ref["matched"]
+    for rid, row in ref["rows"].items():
+        np.testing.assert_array_equal(run.rows[rid], row)
+    exp = expected_outputs(wl)
+    req, pos = run.job_sources()
+    start = _token_starts(run)
+    o = run.o.float().cpu().numpy()
+    want = np.stack([exp[int(run.req_rid[r])][p - start[r]] for r, p in zip(req, pos)])
+    err = np.abs(o - want).max()
+    print(f"[gpu] evicting pool: {len(run.iterations)} launches, max abs err {err:.3g}", flush=True)
+    assert err <= TOL["fp32"]
 
 
 def _token_q(wl, r, pos):
