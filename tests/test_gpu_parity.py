@@ -165,7 +165,7 @@ def test_separate_calls_match_decode_step():
             np.testing.assert_array_equal(x, y)
 
 
-@pytest.mark.parametrize("cfg", CONFIGS[1:], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [c for c in CONFIGS if c.dtype == "bf16"], ids=lambda c: c.name)
 def test_full_size_sampled(cfg):
     """Full-size workloads, default launch configuration (as timed by the
     benchmark), checked on sampled leaf requests plus the first hint."""
