@@ -172,6 +172,9 @@ def run_mixed_bench(args, cfg, wl):
         "roofline_hbm_decode_only": roof(dec_only, "hbm") if dec_only.any() else None,
         "attention_ms_per_job": float(dur.sum() * 1e3),
     }
+    if not args.no_cpu_baseline:
+        print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_mixed(run, tlen, args.cpu_seconds)
     print(json.dumps(line, default=float), flush=True)
 
 
@@ -198,6 +201,84 @@ def measured_traffic(kind: str, workload: str):
     if not m_src or not m_val or m_src.group(1) != kernel_source_digest():
         return None
     return {"bytes_per_launch": int(m_val.group(1)), "source": os.path.relpath(path, ROOT)}
+
+
+def cpu_host_rows():
+    """The oracle's host algorithms timed beside the library's (same inputs
+    as the probes): the cache-aware order of the 128-prompt queue, the
+    global prefix analysis of 128 BatchLLM-shaped prompts (the oracle's token
+    trie; the library's call is timed on all 1,024), and the eviction stream
+    served on a 6,000-slot cache with LFU."""
+    import numpy as np
+    from oracle import TokenTrieCache
+    from oracle import schedule as osch
+    from oracle.prefix_groups import min_processed
+    from workloads import Workload, config_by_name, reuse_stream, waiting_queue
+
+    wl = Workload(config_by_name("batchllm"))
+    out = {}
+    prompts = [[int(t) for t in p] for p in waiting_queue(wl, 128)]
+    t0 = time.perf_counter()
+    osch.lpm_order(TokenTrieCache(10 ** 6), prompts)
+    out["schedule_ms"] = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    min_processed(prompts)
+    out["prefix_groups_128_ms"] = (time.perf_counter() - t0) * 1e3
+    stream, _ = reuse_stream()
+    c = TokenTrieCache(6000, 1, "lfu")
+    t0 = time.perf_counter()
+    for p in stream:
+        m, slots, node = c.match_prefix(p)
+        if node:
+            c.lock(node)
+        new = c.alloc(len(p) - m)
+        k, _ = c.insert(p, list(slots) + new)
+        c.free(new[: k - m])
+        if node:
+            c.unlock(node)
+    out["eviction_stream_s"] = time.perf_counter() - t0
+    return out
+
+
+def cpu_baseline_mixed(run, tlen, seconds: float):
+    """The oracle on the token-batched job, untuned, on this host's cores:
+    its batching of the whole job and its cache model over the whole job,
+    plus attention for the first member requests until `seconds` of
+    attention work; the attention time is scaled to the job by (query, key)
+    pairs."""
+    import numpy as np
+    from oracle.mixed_run import mixed_groups, run_mixed
+    from oracle.run import request_attention
+    from oracle.token_batching import batch_iterations
+
+    wl = run.wl
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    groups, _ = mixed_groups(wl, tlen)
+    batch_iterations(groups, run.s_chunk, run.m_threshold)
+    t_sched = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    run_mixed(wl, run.s_chunk, run.m_threshold, tlen)
+    t_cache = time.perf_counter() - t0
+    mem = wl.phases[1].requests
+    done, t_attn, pairs_done = 0, 0.0, 0
+    while done < len(mem) and t_attn < seconds:
+        r = mem[done]
+        t1 = time.perf_counter()
+        request_attention(wl, r)   # its own tokens and all drawn decode tokens
+        t_attn += time.perf_counter() - t1
+        first = r.prompt_len - r.own_len
+        last = r.prompt_len + r.decode_steps
+        pairs_done += (last * (last + 1) - first * (first + 1)) // 2
+        done += 1
+    _, pos = run.job_sources()
+    pairs_all = int((pos + 1).sum())
+    est = t_sched + t_cache + t_attn * pairs_all / max(pairs_done, 1)
+    return {"value": run.n_tokens / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle: token batching of the whole job ({t_sched:.2f}s), cache model over "
+                      f"the whole job ({t_cache:.2f}s), attention of the first {done} member requests "
+                      f"({t_attn:.2f}s, {pairs_done} query-key pairs) scaled to the job's {pairs_all} pairs; "
+                      f"BLAS threads = host cores"}
 
 
 def cpu_baseline(wl, seconds: float):
@@ -516,6 +597,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        if not args.no_schedule_probe:
+            line["cpu_baseline"]["host_rows"] = cpu_host_rows()
     print(json.dumps(line, default=float), flush=True)
 
 
