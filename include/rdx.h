@@ -323,8 +323,10 @@ int rdx_plan_get_info(const rdx_plan* plan, rdx_plan_info* out);
 /* Copy the plan to dev_plan (device, >= device_bytes) on `stream` and write
  * the batch's page-table entries into page_table (device int32
  * [page_table_rows][ld]).  The plan stages uploads through a ring of 4
- * pinned host buffers; the call blocks only while the upload made 4 calls
- * earlier has not left its buffer yet.  Errors: EINVAL, EDEVICE. */
+ * pinned host buffers, read by a copy kernel through their device mapping
+ * (no DMA copy); the call blocks only while the upload made 4 calls earlier
+ * has not left its buffer yet, and grows the ring (pinned allocations) when
+ * a plan outgrows it.  Errors: EINVAL, EDEVICE. */
 int rdx_plan_upload(rdx_plan* plan, void* dev_plan, int64_t dev_plan_bytes,
                     int32_t* page_table, int64_t page_table_rows, void* stream);
 
@@ -334,7 +336,8 @@ int rdx_plan_upload(rdx_plan* plan, void* dev_plan, int64_t dev_plan_bytes,
  *               workgroup needs first (block count, tile and contribution
  *               fields, first job) -- one per key chunk; the launch runs
  *               item i for KV head h as workgroup i * Hkv + h
- *   tile    [8] tok_begin, n_tok, n_contrib, contrib_begin, counter (-1 = no merge), 0,0,0
+ *   tile    [8] tok_begin, n_tok, n_contrib, contrib_begin, split index
+ *               (-1 = not split), merge-list base, 0, 0
  *   job     [8] page_row, key_begin, key_end, tok_lo, tok_hi, causal, 0, 0
  *   token   [2] q_index, position
  *   contrib [4] tok_lo, tok_hi, ws_token_base, 0 */
