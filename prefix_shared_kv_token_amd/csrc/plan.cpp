@@ -278,9 +278,19 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   // default launch size the split aims for (about one round of workgroups):
   // extend splits only when fewer work items than that exist -- 256 for the
   // 256-row kernel (one workgroup per CU), 512 for the 128-row one (two);
-  // decode aims for ~2 per CU (measured best: larger chunks amortise the Q
-  // load and the partial write, smaller ones add merge work)
+  // decode aims for whole workgroups per CU on every XCD (a launch whose
+  // items leave some CUs of an XCD one workgroup more than others runs at
+  // the pace of those): two per CU when an item would be short (the second
+  // workgroup's stream covers the first's start-up), one per CU when each
+  // item gets at least 32 blocks that way (the start-up is amortised, and
+  // half the items means half the partials to write and merge).  Measured on
+  // MI355X: 1,000-key prefix + 64 short requests best at 512 (items of 9
+  // blocks), 16,000-key prefixes at 256 (items of 42 blocks)
   int64_t target = target_items > 0 ? target_items : (kind == RDX_PLAN_EXTEND && tile_rows == 256 ? 256 : 512);
+  if (target_items <= 0 && kind == RDX_PLAN_DECODE) {
+    const int64_t per_kvh1 = std::max<int64_t>(1, 256 / hkv);
+    if ((total_cost + per_kvh1 - 1) / per_kvh1 >= 32) target = 256;
+  }
   int64_t chunk = INT64_MAX;
   if ((int64_t)ntiles * hkv < target && total_cost > 0) {
     int64_t per_kvh = std::max<int64_t>(1, target / hkv);
