@@ -295,6 +295,32 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   if ((int64_t)ntiles * hkv < target && total_cost > 0) {
     int64_t per_kvh = std::max<int64_t>(1, target / hkv);
     chunk = std::max<int64_t>(1, (total_cost + per_kvh - 1) / per_kvh);  // blocks per item
+    // a tile is cut into ceil(cost / chunk) items; rounding per tile can
+    // overshoot the target and start a second round of workgroups for a few
+    // of them, so take the smallest chunk that stays within it (the item
+    // count only falls as the chunk grows; at the largest tile cost it is
+    // the tile count, below the target)
+    static thread_local std::vector<int64_t> tcost;
+    tcost.assign(ntiles, 0);
+    int64_t hi = 1;
+    for (int t = 0; t < ntiles; ++t) {
+      for (int jx = sc.tile_job_begin[t]; jx < sc.tile_job_begin[t + 1]; ++jx)
+        tcost[t] += (sc.tjobs[jx].k1 - sc.tjobs[jx].k0 + kKeyBlock - 1) / kKeyBlock;
+      hi = std::max(hi, tcost[t]);
+    }
+    auto count = [&](int64_t c) {
+      int64_t n = 0;
+      for (int t = 0; t < ntiles; ++t) n += std::max<int64_t>(1, (tcost[t] + c - 1) / c);
+      return n;
+    };
+    if (count(chunk) > per_kvh) {
+      int64_t lo = chunk;  // count(lo) > per_kvh >= count(hi)
+      while (hi - lo > 1) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        (count(mid) > per_kvh ? lo : hi) = mid;
+      }
+      chunk = hi;
+    }
   }
   jobs.clear();
   contribs.clear();

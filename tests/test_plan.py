@@ -166,3 +166,36 @@ def test_decode_items_are_sized_in_blocks():
     assert [int(it[4]) for it in v["items"]] == per_item
     assert max(per_item) <= -(-total // (target // 2))
     assert sum(per_item) == total
+
+
+def test_split_stays_within_the_item_target():
+    """Five small sharing groups and one long one (decode, 32 KV heads: the
+    default target of 512 items is 16 per head).  Cutting every tile by the
+    same block count rounds up per tile (5 x 1 + 15 = 20 items per head); the
+    planner takes the smallest block count whose items fit in 16, so no
+    workgroup waits for a second round.  Coverage stays exact."""
+    hkv = 32
+    prefixes = [np.arange(64, dtype=np.int32) + 1000 * (g + 1) for g in range(5)]
+    prefixes.append(np.arange(64 * 200, dtype=np.int32) + 100_000)
+    tree = rdx.Tree(64 * 300)
+    for p in prefixes:
+        m, slots, node = tree.match_prefix(p)
+        row = np.concatenate([slots, tree.alloc(len(p) - m)])
+        tree.insert(p, row)
+    reqs = []
+    for g, p in enumerate(prefixes):
+        for i in range(2):
+            prompt = np.concatenate([p, [7 + i + 10 * g]]).astype(np.int32)
+            m, slots, node = tree.match_prefix(prompt)
+            tree.lock(node)
+            reqs.append((prompt, m, node, np.concatenate([slots, tree.alloc(len(prompt) - m)])))
+    desc = rdx.attn_desc(rdx.BF16, hkv, hkv, 128, 64 * 300)
+    rows = list(range(len(reqs)))
+    kv1 = [len(p) + 1 for p, *_ in reqs]
+    plan = rdx.Plan(desc, rdx.PLAN_DECODE)
+    plan.build(tree, [n for _, _, n, _ in reqs], rows, kv1, [1] * len(reqs), [len(p) for p, *_ in reqs],
+               tree.alloc(len(reqs)), 64 * 201 + 2)
+    info = plan.info()
+    assert info["num_tiles"] == 6 and info["num_split_tiles"] >= 1
+    assert info["num_items"] == 512, info["num_items"]   # 16 per head: 5 small tiles whole + 11 pieces
+    _check_coverage(plan, kv1, [1] * len(reqs), rows, hkv)
