@@ -291,36 +291,51 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     const int64_t per_kvh1 = std::max<int64_t>(1, 256 / hkv);
     if ((total_cost + per_kvh1 - 1) / per_kvh1 >= 32) target = 256;
   }
-  int64_t chunk = INT64_MAX;
+  // blocks per tile
+  static thread_local std::vector<int64_t> tcost;
+  tcost.assign(ntiles, 0);
+  int64_t max_cost = 1;
+  for (int t = 0; t < ntiles; ++t) {
+    for (int jx = sc.tile_job_begin[t]; jx < sc.tile_job_begin[t + 1]; ++jx)
+      tcost[t] += (sc.tjobs[jx].k1 - sc.tjobs[jx].k0 + kKeyBlock - 1) / kKeyBlock;
+    max_cost = std::max(max_cost, tcost[t]);
+  }
+  int64_t chunk = INT64_MAX;   // blocks per item of tiles [0, tail_from)
+  int tail_from = ntiles;      // tiles [tail_from, ntiles) are cut into tail_pieces items each
+  int64_t tail_pieces = 1;
+  const int64_t per_kvh = std::max<int64_t>(1, target / hkv);
   if ((int64_t)ntiles * hkv < target && total_cost > 0) {
-    int64_t per_kvh = std::max<int64_t>(1, target / hkv);
-    chunk = std::max<int64_t>(1, (total_cost + per_kvh - 1) / per_kvh);  // blocks per item
+    chunk = std::max<int64_t>(1, (total_cost + per_kvh - 1) / per_kvh);
     // a tile is cut into ceil(cost / chunk) items; rounding per tile can
     // overshoot the target and start a second round of workgroups for a few
     // of them, so take the smallest chunk that stays within it (the item
     // count only falls as the chunk grows; at the largest tile cost it is
     // the tile count, below the target)
-    static thread_local std::vector<int64_t> tcost;
-    tcost.assign(ntiles, 0);
-    int64_t hi = 1;
-    for (int t = 0; t < ntiles; ++t) {
-      for (int jx = sc.tile_job_begin[t]; jx < sc.tile_job_begin[t + 1]; ++jx)
-        tcost[t] += (sc.tjobs[jx].k1 - sc.tjobs[jx].k0 + kKeyBlock - 1) / kKeyBlock;
-      hi = std::max(hi, tcost[t]);
-    }
     auto count = [&](int64_t c) {
       int64_t n = 0;
       for (int t = 0; t < ntiles; ++t) n += std::max<int64_t>(1, (tcost[t] + c - 1) / c);
       return n;
     };
     if (count(chunk) > per_kvh) {
-      int64_t lo = chunk;  // count(lo) > per_kvh >= count(hi)
+      int64_t lo = chunk, hi = max_cost;  // count(lo) > per_kvh >= count(hi)
       while (hi - lo > 1) {
         const int64_t mid = lo + (hi - lo) / 2;
         (count(mid) > per_kvh ? lo : hi) = mid;
       }
       chunk = hi;
     }
+  } else if (ntiles > per_kvh && ntiles % per_kvh != 0 && per_kvh / (ntiles % per_kvh) >= 4) {
+    // more tiles than one round of workgroups and a short last round of e
+    // tiles per KV head: that round would leave most CUs idle for a whole
+    // tile's time.  The last e tiles (dispatched last) are cut into
+    // per_kvh / e pieces each, so the last round is full with pieces of a
+    // quarter of a tile or less.  Measured on MI355X (extend, 256-row
+    // tiles): 10 tiles per head on 8 slots, last 2 in quarters, 116 -> 98 us
+    // with the merge; 48 on 32, last 16 in halves, no gain (134 -> 137 us:
+    // the merge and the partial writes eat the half round)
+    const int64_t e = ntiles % per_kvh;
+    tail_from = ntiles - (int)e;
+    tail_pieces = per_kvh / e;
   }
   jobs.clear();
   contribs.clear();
@@ -338,15 +353,16 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     int32_t* tl = &tiles[t * kTileWords];
     mine.clear();
     int64_t cur = 0;
+    const int64_t tchunk = t < tail_from ? chunk : std::max<int64_t>(1, (tcost[t] + tail_pieces - 1) / tail_pieces);
     for (int jx = sc.tile_job_begin[t]; jx < sc.tile_job_begin[t + 1]; ++jx) {
       const Job& j = sc.tjobs[jx];
       for (int64_t a = j.k0; a < j.k1;) {
-        int64_t room = chunk - cur;
+        int64_t room = tchunk - cur;
         if (room <= 0 || mine.empty()) {
           mine.push_back({t, (int32_t)(jobs.size() / kJobWords), (int32_t)(jobs.size() / kJobWords),
                           (int32_t)mine.size(), 0, 0});
           cur = 0;
-          room = chunk;
+          room = tchunk;
         }
         // room is in blocks: the piece takes whole blocks of the job
         const int64_t e = room >= ((int64_t)j.k1 - a + kKeyBlock - 1) / kKeyBlock ? (int64_t)j.k1 : a + room * kKeyBlock;

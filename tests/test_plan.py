@@ -66,11 +66,14 @@ def _check_coverage(plan, kv_len, q_len, rows, hkv):
                     cover[key] = cover.get(key, 0) + 1
                 # the job reads the row of a request that shares these positions
                 assert j[0] in row_of_req
+    per_row = {}
+    for (a, b, p), c in cover.items():
+        per_row.setdefault((a, b), []).extend([p] * c)
     for qi in range(n_tok):
         r = int(np.searchsorted(q_off, qi, side="right") - 1)
         pos = kv_len[r] - q_len[r] + (qi - q_off[r])
         for h in range(hkv):
-            got = sorted(p for (a, b, p), c in cover.items() if a == qi and b == h for _ in range(c))
+            got = sorted(per_row.get((qi, h), []))
             assert got == list(range(pos + 1)), (qi, h)
     return v
 
@@ -169,12 +172,12 @@ def test_decode_items_are_sized_in_blocks():
 
 
 def test_split_stays_within_the_item_target():
-    """Five small sharing groups and one long one (decode, 32 KV heads: the
-    default target of 512 items is 16 per head).  Cutting every tile by the
-    same block count rounds up per tile (5 x 1 + 15 = 20 items per head); the
-    planner takes the smallest block count whose items fit in 16, so no
-    workgroup waits for a second round.  Coverage stays exact."""
-    hkv = 32
+    """Five small sharing groups and one long one (decode, 2 KV heads, a
+    target of 32 items: 16 per head).  Cutting every tile by the same block
+    count rounds up per tile (5 x 1 + 15 = 20 items per head); the planner
+    takes the smallest block count whose items fit in 16, so no workgroup
+    waits for a second round.  Coverage stays exact."""
+    hkv = 2
     prefixes = [np.arange(64, dtype=np.int32) + 1000 * (g + 1) for g in range(5)]
     prefixes.append(np.arange(64 * 200, dtype=np.int32) + 100_000)
     tree = rdx.Tree(64 * 300)
@@ -192,10 +195,37 @@ def test_split_stays_within_the_item_target():
     desc = rdx.attn_desc(rdx.BF16, hkv, hkv, 128, 64 * 300)
     rows = list(range(len(reqs)))
     kv1 = [len(p) + 1 for p, *_ in reqs]
-    plan = rdx.Plan(desc, rdx.PLAN_DECODE)
+    plan = rdx.Plan(desc, rdx.PLAN_DECODE, 32)
     plan.build(tree, [n for _, _, n, _ in reqs], rows, kv1, [1] * len(reqs), [len(p) for p, *_ in reqs],
                tree.alloc(len(reqs)), 64 * 201 + 2)
     info = plan.info()
     assert info["num_tiles"] == 6 and info["num_split_tiles"] >= 1
-    assert info["num_items"] == 512, info["num_items"]   # 16 per head: 5 small tiles whole + 11 pieces
+    assert info["num_items"] == 32, info["num_items"]   # 16 per head: 5 small tiles whole + 11 pieces
     _check_coverage(plan, kv1, [1] * len(reqs), rows, hkv)
+
+
+def test_partial_last_round_is_cut_into_pieces():
+    """Extend with 5 tiles per KV head on a target of 4 items per head: one
+    full round, then 1 tile that would leave three quarters of the second
+    round idle for a whole tile.  That last tile is cut into quarters (4
+    pieces fill the round), the others stay whole; coverage stays exact."""
+    cfg = config_by_name("helpdesk").replace(levels=((1, 512), (4, 80)), decode_steps=1, n_q_heads=8, n_kv_heads=2)
+    wl, tree, phases = _admit_phases(cfg)
+    reqs = phases[-1]
+    desc = rdx.attn_desc(rdx.BF16, 8, 2, 128, cfg.total_tokens())
+    plan = rdx.Plan(desc, rdx.PLAN_EXTEND, 8)
+    kv_len = [len(p) for p, *_ in reqs]
+    q_len = [len(p) - m for p, m, *_ in reqs]
+    rows = list(range(len(reqs)))
+    new = np.concatenate([row[m:] for p, m, n, row in reqs])
+    plan.build(tree, [n for _, _, n, _ in reqs], rows, kv_len, q_len, [0] * len(reqs), new, cfg.max_seq_len)
+    info = plan.info()
+    assert sum(q_len) * 4 == 1280 and info["num_tiles"] == 5
+    assert info["num_items"] == 2 * (4 + 4)
+    assert info["num_split_tiles"] == 1
+    v = _check_coverage(plan, kv_len, q_len, rows, 2)
+    assert [int(t[2]) for t in v["tiles"]] == [1, 1, 1, 1, 4]
+    # halves do not pay: 5 tiles on 3 slots per head (2 left over) stay whole
+    plan2 = rdx.Plan(desc, rdx.PLAN_EXTEND, 6)
+    plan2.build(tree, [n for _, _, n, _ in reqs], rows, kv_len, q_len, [0] * len(reqs), new, cfg.max_seq_len)
+    assert plan2.info()["num_items"] == 2 * 5 and plan2.info()["num_split_tiles"] == 0
