@@ -106,6 +106,16 @@ def test_edge_shapes(base, kw, items):
     run_and_check(config_by_name(base).replace(**kw), extend_items=items, decode_items=items)
 
 
+def test_short_last_round_cut_into_quarters():
+    """Member extend of 5 wide tiles per KV head on 4 items per head: the
+    fifth tile runs as 4 quarter pieces merged by LSE; the decode tile is
+    split into 4 items.  Every output against the oracle."""
+    cfg = config_by_name("helpdesk").replace(levels=((1, 512), (4, 80)), n_q_heads=8, n_kv_heads=2, decode_steps=3)
+    run, out, ref = run_and_check(cfg, extend_items=8, decode_items=8)
+    info = out["plan_info"][1]
+    assert info["num_tiles"] == 5 and info["num_split_tiles"] == 1 and info["num_items"] == 2 * 8
+
+
 def test_fragmented_pool_bf16():
     cfg = config_by_name("multilevel").replace(levels=((1, 100), (2, 40), (3, 11)), decode_steps=4)
     run_and_check(cfg, hole_seed=11, extra_slots=333)
