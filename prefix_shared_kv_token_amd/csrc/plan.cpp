@@ -294,35 +294,35 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   // blocks per tile
   static thread_local std::vector<int64_t> tcost;
   tcost.assign(ntiles, 0);
-  int64_t max_cost = 1;
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = 0; t < ntiles; ++t)
     for (int jx = sc.tile_job_begin[t]; jx < sc.tile_job_begin[t + 1]; ++jx)
       tcost[t] += (sc.tjobs[jx].k1 - sc.tjobs[jx].k0 + kKeyBlock - 1) / kKeyBlock;
-    max_cost = std::max(max_cost, tcost[t]);
-  }
-  int64_t chunk = INT64_MAX;   // blocks per item of tiles [0, tail_from)
-  int tail_from = ntiles;      // tiles [tail_from, ntiles) are cut into tail_pieces items each
-  int64_t tail_pieces = 1;
+  // items per tile (each tile's blocks are cut into that many runs of
+  // nearly equal length)
+  static thread_local std::vector<int64_t> npieces;
+  npieces.assign(ntiles, 1);
   const int64_t per_kvh = std::max<int64_t>(1, target / hkv);
   if ((int64_t)ntiles * hkv < target && total_cost > 0) {
-    chunk = std::max<int64_t>(1, (total_cost + per_kvh - 1) / per_kvh);
-    // a tile is cut into ceil(cost / chunk) items; rounding per tile can
-    // overshoot the target and start a second round of workgroups for a few
-    // of them, so take the smallest chunk that stays within it (the item
-    // count only falls as the chunk grows; at the largest tile cost it is
-    // the tile count, below the target)
-    auto count = [&](int64_t c) {
-      int64_t n = 0;
-      for (int t = 0; t < ntiles; ++t) n += std::max<int64_t>(1, (tcost[t] + c - 1) / c);
-      return n;
-    };
-    if (count(chunk) > per_kvh) {
-      int64_t lo = chunk, hi = max_cost;  // count(lo) > per_kvh >= count(hi)
-      while (hi - lo > 1) {
-        const int64_t mid = lo + (hi - lo) / 2;
-        (count(mid) > per_kvh ? lo : hi) = mid;
-      }
-      chunk = hi;
+    // fewer tiles than the target: hand out the target's items one at a
+    // time to the tile whose pieces are currently the longest (the launch
+    // takes as long as its longest item), never more pieces than blocks.
+    // The count is exact, so items per XCD stay a whole number per CU
+    // (an item count a little over a multiple of the CU count would start a
+    // second round of workgroups for a few of them)
+    static thread_local std::vector<std::pair<int64_t, int>> heap;
+    heap.clear();
+    auto piece = [&](int t) { return (tcost[t] + npieces[t] - 1) / npieces[t]; };
+    for (int t = 0; t < ntiles; ++t) heap.push_back({piece(t), t});
+    std::make_heap(heap.begin(), heap.end());
+    for (int64_t given = ntiles; given < per_kvh && !heap.empty();) {
+      std::pop_heap(heap.begin(), heap.end());
+      const int t = heap.back().second;
+      heap.pop_back();
+      if (npieces[t] >= tcost[t]) continue;  // one block per piece: no further cut
+      ++npieces[t];
+      ++given;
+      heap.push_back({piece(t), t});
+      std::push_heap(heap.begin(), heap.end());
     }
   } else if (ntiles > per_kvh && ntiles % per_kvh != 0 && per_kvh / (ntiles % per_kvh) >= 4) {
     // more tiles than one round of workgroups and a short last round of e
@@ -334,8 +334,7 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     // with the merge; 48 on 32, last 16 in halves, no gain (134 -> 137 us:
     // the merge and the partial writes eat the half round)
     const int64_t e = ntiles % per_kvh;
-    tail_from = ntiles - (int)e;
-    tail_pieces = per_kvh / e;
+    for (int t = ntiles - (int)e; t < ntiles; ++t) npieces[t] = std::min(per_kvh / e, std::max<int64_t>(1, tcost[t]));
   }
   jobs.clear();
   contribs.clear();
@@ -352,17 +351,18 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   for (int t = 0; t < ntiles; ++t) {
     int32_t* tl = &tiles[t * kTileWords];
     mine.clear();
-    int64_t cur = 0;
-    const int64_t tchunk = t < tail_from ? chunk : std::max<int64_t>(1, (tcost[t] + tail_pieces - 1) / tail_pieces);
+    // item i of the tile ends at block floor((i + 1) cost / n)
+    const int64_t np = npieces[t], ct = tcost[t];
+    int64_t used = 0;
+    auto item_end = [&](int64_t i) { return (i + 1) * ct / np; };
     for (int jx = sc.tile_job_begin[t]; jx < sc.tile_job_begin[t + 1]; ++jx) {
       const Job& j = sc.tjobs[jx];
       for (int64_t a = j.k0; a < j.k1;) {
-        int64_t room = tchunk - cur;
-        if (room <= 0 || mine.empty()) {
+        int64_t room = mine.empty() ? 0 : item_end((int64_t)mine.size() - 1) - used;
+        if (room <= 0) {
           mine.push_back({t, (int32_t)(jobs.size() / kJobWords), (int32_t)(jobs.size() / kJobWords),
                           (int32_t)mine.size(), 0, 0});
-          cur = 0;
-          room = tchunk;
+          room = item_end((int64_t)mine.size() - 1) - used;
         }
         // room is in blocks: the piece takes whole blocks of the job
         const int64_t e = room >= ((int64_t)j.k1 - a + kKeyBlock - 1) / kKeyBlock ? (int64_t)j.k1 : a + room * kKeyBlock;
@@ -371,7 +371,7 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
         mine.back().je++;
         mine.back().cost += nb;
         mine.back().keys += e - a;
-        cur += nb;
+        used += nb;
         a = e;
       }
     }

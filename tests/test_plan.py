@@ -174,9 +174,10 @@ def test_decode_items_are_sized_in_blocks():
 def test_split_stays_within_the_item_target():
     """Five small sharing groups and one long one (decode, 2 KV heads, a
     target of 32 items: 16 per head).  Cutting every tile by the same block
-    count rounds up per tile (5 x 1 + 15 = 20 items per head); the planner
-    takes the smallest block count whose items fit in 16, so no workgroup
-    waits for a second round.  Coverage stays exact."""
+    count would round up per tile (5 x 1 + 15 = 20 items per head) and start
+    a second round for a few workgroups; the planner hands the 16 items out
+    one by one to the tile with the longest pieces, so the count is exact
+    and the long tile's pieces are even.  Coverage stays exact."""
     hkv = 2
     prefixes = [np.arange(64, dtype=np.int32) + 1000 * (g + 1) for g in range(5)]
     prefixes.append(np.arange(64 * 200, dtype=np.int32) + 100_000)
@@ -201,7 +202,10 @@ def test_split_stays_within_the_item_target():
     info = plan.info()
     assert info["num_tiles"] == 6 and info["num_split_tiles"] >= 1
     assert info["num_items"] == 32, info["num_items"]   # 16 per head: 5 small tiles whole + 11 pieces
-    _check_coverage(plan, kv1, [1] * len(reqs), rows, hkv)
+    v = _check_coverage(plan, kv1, [1] * len(reqs), rows, hkv)
+    # the long tile's 11 pieces are of nearly equal length (202 blocks: 18 or 19 each)
+    big = [int(it[4]) for it in v["items"] if v["tiles"][it[0]][2] > 1]
+    assert len(big) == 11 and sum(big) == 202 and max(big) - min(big) <= 1, big
 
 
 def test_partial_last_round_is_cut_into_pieces():
