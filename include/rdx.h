@@ -294,9 +294,15 @@ typedef struct rdx_batch {
   const int32_t* new_slots;
 } rdx_batch;
 
-/* kind: RDX_PLAN_EXTEND or RDX_PLAN_DECODE; target_items: the launch size the
- * planner splits key ranges towards (0 = default).  Errors: EINVAL,
- * EUNSUPPORTED. */
+/* kind: RDX_PLAN_EXTEND or RDX_PLAN_DECODE; target_items: the launch size
+ * (workgroups = item records x Hkv) the planner splits key ranges towards;
+ * 0 = the default for MI355X's 256 CUs: 256 for the 256-row extend kernel,
+ * 512 for the others, 256 for decode launches whose items would each get 32
+ * or more 64-key blocks that way.  When a launch has fewer tiles than the
+ * target, the target's items are handed out to the tiles with the longest
+ * pieces (never more than the target); when a launch runs more than one
+ * round of tiles with a short last round, its last tiles are cut into
+ * pieces of a quarter tile or less.  Errors: EINVAL, EUNSUPPORTED. */
 int rdx_plan_create(const rdx_attn_desc* desc, int32_t kind, int32_t target_items, rdx_plan** out);
 void rdx_plan_destroy(rdx_plan* plan);
 
