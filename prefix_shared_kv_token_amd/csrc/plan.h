@@ -61,7 +61,7 @@ struct Plan {
   // upload staging, owned by the plan: a ring of pinned host buffers, each
   // with the event of the last copy out of it, so the host can prepare the
   // next uploads while earlier ones are still queued
-  static constexpr int kStages = 4;
+  static constexpr int kStages = 8;
   struct Stage {
     void* pinned = nullptr;
     void* pinned_dev = nullptr;  // the same memory as the device addresses it
