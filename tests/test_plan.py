@@ -233,3 +233,26 @@ def test_partial_last_round_is_cut_into_pieces():
     plan2 = rdx.Plan(desc, rdx.PLAN_EXTEND, 6)
     plan2.build(tree, [n for _, _, n, _ in reqs], rows, kv_len, q_len, [0] * len(reqs), new, cfg.max_seq_len)
     assert plan2.info()["num_items"] == 2 * 5 and plan2.info()["num_split_tiles"] == 0
+
+
+@pytest.mark.parametrize("name,items", [("helpdesk", 512), ("longprefix", 256), ("multilevel", 512),
+                                        ("batchllm", 512)])
+def test_default_decode_launch_size(name, items):
+    """Default decode split of the four workloads' first decode step: whole
+    workgroups per CU on MI355X's 256 CUs -- two per CU when items are short
+    (Helpdesk: 16 items of 9 blocks per head; Multi-level), one per CU when
+    each item still gets 32+ blocks (Long-prefix: 32 items of ~41 blocks per
+    head); BatchLLM's 64 tiles x 8 heads need no split."""
+    cfg = config_by_name(name)
+    wl, tree, phases = _admit_phases(cfg)
+    reqs = phases[-1]
+    desc = rdx.attn_desc(rdx.BF16, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.total_tokens())
+    plan = rdx.Plan(desc, rdx.PLAN_DECODE)
+    kv1 = [len(p) + 1 for p, *_ in reqs]
+    plan.build(tree, [n for _, _, n, _ in reqs], list(range(len(reqs))), kv1, [1] * len(reqs),
+               [len(p) for p, *_ in reqs], tree.alloc(len(reqs)), cfg.max_seq_len)
+    info = plan.info()
+    assert info["num_items"] == items
+    if name != "batchllm":
+        blocks = [int(it[4]) for it in plan.view()["items"]]
+        assert max(blocks) - min(blocks) <= 1 or info["num_tiles"] > 1
