@@ -486,7 +486,8 @@ int rdx_job_launch(rdx_job* job, const rdx_attn_desc* desc, const rdx_step_io* i
  * attention kernel's duration in milliseconds to out_attn_ms, the merge
  * kernel's (0 when none ran) to out_merge_ms (may be NULL) and the kind
  * (RDX_PLAN_EXTEND / RDX_PLAN_DECODE) to out_kind; it sets *out_n and stops
- * recording.  Errors: EINVAL, EDEVICE. */
+ * recording.  The recording is process-wide (launches from every thread and
+ * plan count); one recording at a time.  Errors: EINVAL, EDEVICE. */
 int rdx_timing_begin(int32_t cap);
 int rdx_timing_read(float* out_attn_ms, float* out_merge_ms, int32_t* out_kind, int32_t cap,
                     int32_t* out_n);
