@@ -107,13 +107,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
       m = a.ws_ml[(int64_t)w * 2];
       l = a.ws_ml[(int64_t)w * 2 + 1];
     }
+    // only the partials this row has are read (lanes of rows with fewer
+    // partials, or whole waves past every row's count, issue no load)
     float4 ov[16][kV4];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int wj = __shfl(w, j, 16);
       const float4* src = reinterpret_cast<const float4*>(a.ws_o + (int64_t)wj * D + part * kPer);
 #pragma unroll
-      for (int e = 0; e < kV4; ++e) ov[j][e] = j < cnt ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int e = 0; e < kV4; ++e) ov[j][e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < cnt) {
+#pragma unroll
+        for (int e = 0; e < kV4; ++e) ov[j][e] = src[e];
+      }
     }
     float bm = l > 0.f ? m : -INFINITY;
 #pragma unroll
