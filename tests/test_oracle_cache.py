@@ -212,3 +212,94 @@ def test_error_paths_leave_state_unchanged():
     with pytest.raises(CacheError) as e:
         cache.free(priv)                  # double free
     assert e.value.code == ESTATE
+
+
+# ---------------------------------------------------------------- slot order
+# Reading of the free-slot order (the pages are silent): allocation hands out
+# the n smallest free slot ids in ascending order, and slots freed by the
+# caller or by eviction go back into that ordered set.  The expected ids
+# below are worked out by hand from that reading.  The same script run on
+# a cache whose free list is a stack (last freed first) or a queue (first
+# freed first) -- both planted here on the CPU -- gives other ids.
+
+def _slot_script(c):
+    """alloc/insert/free/evict sequence -> every alloc's result."""
+    got = [c.alloc(3)]                          # [0, 1, 2]
+    c.insert([10, 11, 12], got[0])              # leaf A (clock 1)
+    got.append(c.alloc(2))                      # [3, 4]
+    c.insert([20, 21], got[1][::-1])            # leaf B (clock 2), slots [4, 3]
+    # free {5, 6, 7}; 5 asked: the 2-slot shortfall evicts the older leaf A
+    # whole (3 slots, more than asked) and its slots rejoin the free set
+    got.append(c.alloc(5))                      # [0, 1, 2, 5, 6]
+    c.free([2])
+    c.free([0])
+    got.append(c.alloc(3))                      # [0, 2, 7]
+    c.free([6])
+    c.free([1])
+    c.free([5])
+    got.append(c.alloc(2))                      # [1, 5]
+    return got
+
+
+SLOT_SCRIPT_EXPECTED = [[0, 1, 2], [3, 4], [0, 1, 2, 5, 6], [0, 2, 7], [1, 5]]
+
+
+def test_alloc_returns_smallest_free_ids_ascending():
+    c = TokenTrieCache(8)
+    assert _slot_script(c) == SLOT_SCRIPT_EXPECTED
+    assert c.evictions == 1 and c.resident_sequences() == [[20, 21]]
+    assert c.node_info(2)["slots"] == [4, 3]
+
+
+class _ListFreeCache(TokenTrieCache):
+    """Planted mistake: the free set kept as a list, taken from the back
+    (stack) or the front (queue) instead of smallest id first."""
+
+    def __init__(self, n, mode):
+        super().__init__(n)
+        self.mode = mode
+        self.free_heap = list(range(n)) if mode == "queue" else list(range(n - 1, -1, -1))
+
+    def alloc(self, n):
+        import oracle.cache_model as cm
+
+        while len(self.free_heap) < n:
+            self._evict_one()
+        out = [self.free_heap.pop() if self.mode == "stack" else self.free_heap.pop(0) for _ in range(n)]
+        for s in out:
+            self.state[s] = cm._PRIVATE
+        return out
+
+
+@pytest.mark.parametrize("mode", ["stack", "queue"])
+def test_slot_script_rejects_list_free_sets(mode, monkeypatch):
+    import oracle.cache_model as cm
+    c = _ListFreeCache(8, mode)
+    # eviction and free push onto the list's end (where a stack pops)
+    monkeypatch.setattr(cm.heapq, "heappush", lambda h, x: h.append(x))
+    try:
+        got = _slot_script(c)
+    except CacheError:     # the script's frees then hit a slot that is not private
+        got = None
+    assert got != SLOT_SCRIPT_EXPECTED
+
+
+def test_decode_steps_take_slots_in_batch_order():
+    """A small phase-structured workload worked by hand: a 3-token hint
+    prefix, two members of 2 tokens each, 2 decode steps.  Every slot id of
+    every page-table row follows from ascending allocation, one alloc per
+    request at admission in batch order, one alloc(R) per decode step dealt
+    to the requests in batch order."""
+    from oracle import run_workload
+    from workloads import Workload, config_by_name
+
+    cfg = config_by_name("tiny").replace(levels=((1, 3), (2, 2)), decode_steps=2)
+    wl = Workload(cfg)
+    res = run_workload(wl, attention_for=())
+    hint = wl.phases[0].requests[0]
+    r0, r1 = wl.phases[1].requests
+    np.testing.assert_array_equal(res.rows[hint.rid], [0, 1, 2])
+    # admission: r0 gets [3, 4], r1 gets [5, 6]; step 0: alloc(2) = [7, 8];
+    # step 1: alloc(2) = [9, 10]
+    np.testing.assert_array_equal(res.rows[r0.rid], [0, 1, 2, 3, 4, 7, 9])
+    np.testing.assert_array_equal(res.rows[r1.rid], [0, 1, 2, 5, 6, 8, 10])
