@@ -10,11 +10,12 @@ Passages followed (BatchLLM explainer):
     queue first (one token per request already decoding), then the
     distinct-prompt queue (requests whose common prefix is processed), then
     the common-prefix queue (prefixes of groups not yet prefilled);
-  * Memory-centric Token Batching: the batch is bounded by KV memory, not by
-    a request count.  Start from the KV memory of the decoding requests, add
-    their decode tokens, then add prefill chunks of at most s_chunk tokens
-    (memory: two entries, K and V, per token) in queue order, stopping at the
-    first chunk that would take the memory above M_threshold.
+  * Memory-centric Token Batching: an iteration's batch is bounded by the KV
+    memory it needs, not by a request count.  Read here as: every decoding
+    request's token is in the batch; the prefill chunks (at most s_chunk
+    tokens each, two KV entries per token) come from the head of the queue,
+    as many as fit beside the memory the decoding requests hold under
+    M_threshold.
 
 Readings of points the pages leave open (the product follows the same):
   * R_group = 1 / (L_prefix + sum of L_distinct) as printed: groups run in
@@ -23,12 +24,12 @@ Readings of points the pages leave open (the product follows the same):
     prefix once (it is shared, the point of prefix sharing), plus each
     decoding request's distinct prompt and the tokens it generated so far,
     before this iteration's token; decode tokens are always taken and add no
-    memory in that iteration (as in the sketch); requests still in prefill
-    are not counted;
+    memory in that iteration; requests still in prefill are not counted;
   * a pending chunk is the next min(s_chunk, remaining) tokens of one
     request's distinct prompt or of one group's prefix; at most one chunk per
-    pending item per iteration; the loop stops at the first chunk that does
-    not fit (later ones are not tried);
+    pending item per iteration; the chunks taken are a head of the queue (a
+    chunk that does not fit ends the batch; later, smaller ones are not
+    tried);
   * a distinct prompt enters the queue the iteration after its group's
     prefix is complete (immediately if the prefix is empty); a request
     decodes from the iteration after its prompt is complete and generates
@@ -41,6 +42,8 @@ Readings of points the pages leave open (the product follows the same):
 from __future__ import annotations
 
 from dataclasses import dataclass
+
+import numpy as np
 
 DECODE, DISTINCT, PREFIX = 0, 1, 2
 
@@ -95,20 +98,18 @@ def batch_iterations(groups, s_chunk: int, m_threshold: int) -> list:
                 pending.append((PREFIX, g, -1, groups[g].prefix_len - pre_done[g], pre_done[g]))
         if not decoding and not pending:
             break
-        batch = []
-        memory = 0
-        for g in {g for g, _ in decoding}:
-            memory += 2 * groups[g].prefix_len
-        for g, j in decoding:
-            memory += 2 * (groups[g].distinct[j] + generated[(g, j)])
-        for g, j in decoding:
-            batch.append((DECODE, g, j, groups[g].prefix_len + groups[g].distinct[j] + generated[(g, j)], 1))
-        for kind, g, j, remaining, begin in pending:
-            c = min(s_chunk, remaining)
-            if memory + 2 * c > m_threshold:
-                break
-            batch.append((kind, g, j, begin, c))
-            memory += 2 * c
+        # KV entries (K and V: two per token) the decoding requests hold
+        held = 2 * (sum(groups[g].prefix_len for g in {g for g, _ in decoding})
+                    + sum(groups[g].distinct[j] + generated[(g, j)] for g, j in decoding))
+        # the batch is bounded by KV memory: the chunks taken are the longest
+        # head of the pending queue whose entries, added to what is held,
+        # stay within M_threshold
+        sizes = [min(s_chunk, remaining) for _, _, _, remaining, _ in pending]
+        need = np.cumsum(2 * np.asarray(sizes, dtype=np.int64)) if sizes else np.zeros(0, np.int64)
+        n_take = int(np.searchsorted(need, m_threshold - held, side="right"))
+        batch = [(DECODE, g, j, groups[g].prefix_len + groups[g].distinct[j] + generated[(g, j)], 1)
+                 for g, j in decoding]
+        batch += [(kind, g, j, begin, c) for (kind, g, j, _, begin), c in zip(pending[:n_take], sizes)]
         assert batch, "no progress"
         for kind, g, j, begin, c in batch:
             if kind == DECODE:

@@ -688,13 +688,18 @@ struct DecPool {
       vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.vp), (short)0, (int)a.pool_bytes, 0x00020000);
     }
   }
-  // byte offset of this thread's first chunk for `slot` (< 0: no row)
+  // byte offset of this thread's first chunk for `slot` (< 0: no row).
+  // 64-bit path: the slot itself, -1 for no row.
   __device__ __forceinline__ uint32_t offset(int slot, uint32_t in_row) const {
     if constexpr (OFF32) return slot >= 0 ? __umul24((uint32_t)slot, row_bytes) + in_row : kNoRow;
-    else return (uint32_t)max(slot, 0);  // 64-bit path: a valid row (masked keys only cost bandwidth)
+    else return (uint32_t)slot;
   }
   template <int CPT>
   __device__ __forceinline__ void load(DecStage<CPT>& st, uint32_t o, uint32_t in_row) const {
+    // 64-bit path, no row: the load still goes out (to row 0, which always
+    // exists: no branch around the load) and the staged values are zeros, so
+    // the masked key's V row enters P.V as 0 whatever row 0 holds
+    const bool none = !OFF32 && (int)o < 0;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       if constexpr (OFF32) {
@@ -703,9 +708,12 @@ struct DecPool {
         st.k[i] = make_uint4(x.x, x.y, x.z, x.w);
         st.v[i] = make_uint4(y.x, y.y, y.z, y.w);
       } else {
-        const int64_t off = (int64_t)o * row_bytes + in_row + 16 * i;
-        st.k[i] = *reinterpret_cast<const uint4*>(kb + off);
-        st.v[i] = *reinterpret_cast<const uint4*>(vb + off);
+        const int64_t off = (int64_t)(none ? 0u : o) * row_bytes + in_row + 16 * i;
+        const uint4 x = *reinterpret_cast<const uint4*>(kb + off);
+        const uint4 y = *reinterpret_cast<const uint4*>(vb + off);
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        st.k[i] = none ? z : x;
+        st.v[i] = none ? z : y;
       }
     }
   }

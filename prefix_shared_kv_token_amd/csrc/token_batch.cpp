@@ -122,24 +122,21 @@ int rdx_batcher_next(rdx_batcher* b, rdx_tb_entry* out, int32_t cap, int32_t* ou
     if (i == 0 || b->group_of[b->decoding[i - 1]] != g) memory += 2 * (int64_t)b->prefix_len[g];
     memory += 2 * ((int64_t)b->distinct_len[m] + b->generated[m]);
   }
+  // The batch is bounded by KV memory (BatchLLM explainer, Memory-centric
+  // Token Batching): beside what the decoding requests hold, the iteration
+  // takes prefill chunks from the head of the queue -- distinct prompts,
+  // then prefixes -- as long as their K/V entries fit under the threshold.
+  const int64_t n2 = (int64_t)b->distinct_q.size(), n3 = (int64_t)b->prefix_q.size();
+  auto remaining = [&](int64_t i) -> int64_t {
+    if (i < n2) return b->distinct_len[b->distinct_q[i]] - b->dist_done[b->distinct_q[i]];
+    const int32_t g = b->prefix_q[i - n2];
+    return b->prefix_len[g] - b->pre_done[g];
+  };
+  int64_t budget = b->threshold - memory;  // K/V entries left for chunks
   int64_t n_chunks = 0;
-  {
-    int64_t mem = memory;
-    const int64_t n2 = (int64_t)b->distinct_q.size(), n3 = (int64_t)b->prefix_q.size();
-    for (int64_t i = 0; i < n2 + n3; ++i) {
-      int64_t rem;
-      if (i < n2) {
-        const int32_t m = b->distinct_q[i];
-        rem = b->distinct_len[m] - b->dist_done[m];
-      } else {
-        const int32_t g = b->prefix_q[i - n2];
-        rem = b->prefix_len[g] - b->pre_done[g];
-      }
-      const int64_t c = std::min<int64_t>(b->s_chunk, rem);
-      if (mem + 2 * c > b->threshold) break;
-      mem += 2 * c;
-      ++n_chunks;
-    }
+  for (; n_chunks < n2 + n3; ++n_chunks) {
+    budget -= 2 * std::min<int64_t>(b->s_chunk, remaining(n_chunks));
+    if (budget < 0) break;
   }
   const int64_t total = nd + n_chunks;
   if (total == 0) return rdx::ok();  // the job is done
@@ -154,7 +151,6 @@ int rdx_batcher_next(rdx_batcher* b, rdx_tb_entry* out, int32_t cap, int32_t* ou
     out[k++] = {RDX_TB_DECODE, g, m, b->prefix_len[g] + b->distinct_len[m] + b->generated[m], 1};
     b->generated[m]++;
   }
-  const int64_t n2 = (int64_t)b->distinct_q.size();
   int64_t taken2 = 0, taken3 = 0;
   for (int64_t i = 0; i < n_chunks; ++i) {
     if (i < n2) {

@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librdx.so")
+# RDX_LIB selects another build of the same ABI (the host-only sanitizer
+# build, whose device entry points fail with RDX_EUNSUPPORTED)
+LIB_PATH = os.environ.get("RDX_LIB") or os.path.join(_HERE, "librdx.so")
 
 OK, EINVAL, ENOSPC, ESTATE, EUNSUPPORTED, EDEVICE, ENOBUFS = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1

@@ -30,7 +30,11 @@ def _fragmenter(num_slots, keep, seed):
     return prep
 
 
-def run_and_check(cfg, sample_leaves=None, extend_items=0, decode_items=0, hole_seed=None, extra_slots=0):
+def run_and_check(cfg, sample_leaves=None, extend_items=0, decode_items=0, hole_seed=None, extra_slots=0,
+                  poison=False, leaf_extra=()):
+    """poison: every pool row starts as NaN, so any key or value the kernels
+    read that the workload never wrote shows up in the outputs.
+    leaf_extra: rids checked besides the sampled leaves (other phases)."""
     torch = _torch()
     from prefix_shared_kv_token_amd.driver import WorkloadRun
 
@@ -39,6 +43,10 @@ def run_and_check(cfg, sample_leaves=None, extend_items=0, decode_items=0, hole_
           f"{cfg.dtype} items={extend_items}/{decode_items} holes={hole_seed}", flush=True)
     run = WorkloadRun(wl, extend_items=extend_items, decode_items=decode_items, hole_seed=hole_seed,
                       extra_slots=extra_slots)
+    if poison:
+        run.rt.k_pool.fill_(float("nan"))
+        run.rt.v_pool.fill_(float("nan"))
+        torch.cuda.synchronize()
     out = run.run()
     torch.cuda.synchronize()
     leaves = wl.leaf_requests
@@ -46,7 +54,7 @@ def run_and_check(cfg, sample_leaves=None, extend_items=0, decode_items=0, hole_
         rids = [r.rid for r in wl.all_requests]
     else:
         idx = sorted(set(int(i) % len(leaves) for i in sample_leaves))
-        rids = [leaves[i].rid for i in idx] + [wl.phases[0].requests[0].rid]
+        rids = [leaves[i].rid for i in idx] + [wl.phases[0].requests[0].rid] + list(leaf_extra)
     prep = _fragmenter(run.num_slots, cfg.total_tokens(), hole_seed) if hole_seed is not None else None
     ref = run_workload(wl, num_slots=run.num_slots, attention_for=rids, prepare=prep)
     # ---- indices: bit-exact ----
@@ -118,7 +126,7 @@ def test_short_last_round_cut_into_quarters():
 
 def test_fragmented_pool_bf16():
     cfg = config_by_name("multilevel").replace(levels=((1, 100), (2, 40), (3, 11)), decode_steps=4)
-    run_and_check(cfg, hole_seed=11, extra_slots=333)
+    run_and_check(cfg, hole_seed=11, extra_slots=333, poison=True)
 
 
 def test_deterministic_and_kv_store_roundtrip():
@@ -147,11 +155,13 @@ def test_deterministic_and_kv_store_roundtrip():
 def test_pool_over_2gib_uses_64bit_addressing():
     """A KV pool of more than 2 GiB per tensor (32 x 128 bf16 heads, ~264k
     slots) takes the kernels' 64-bit address path; the scattered free set puts
-    the workload's pages all over it, past the 2 GiB mark."""
+    the workload's pages all over it, past the 2 GiB mark.  Every pool row
+    starts as NaN: keys past a job's end must not let row 0 (or any other
+    unwritten row) into the outputs."""
     row_bytes = 32 * 128 * 2
     extra = (1 << 31) // row_bytes + 4096
     cfg = config_by_name("helpdesk").replace(levels=((1, 60), (6, 20)), decode_steps=3)
-    run, _, _ = run_and_check(cfg, hole_seed=21, extra_slots=extra)
+    run, _, _ = run_and_check(cfg, hole_seed=21, extra_slots=extra, poison=True)
     assert run.num_slots * row_bytes > (1 << 31)
 
 
