@@ -89,7 +89,10 @@ def _token_q(wl, r, pos):
 
 def test_mixed_batchllm_full_size_sampled():
     """64 groups x 16 (prefix 2,000, distinct 200, up to 64 generated), chunks
-    of 512, KV memory bound a fifth of the job's -- as the benchmark runs it."""
+    of 512, KV memory bound a fifth of the job's -- as the benchmark runs it.
+    Every request's matched length and page-table row against the oracle's
+    cache run (bit-exact); outputs on sampled tokens: one from every launch,
+    48 more at random, the job's first and last."""
     cfg = config_by_name("batchllm")
     wl = Workload(cfg)
     tlen = decode_lengths(wl)
@@ -98,29 +101,30 @@ def test_mixed_batchllm_full_size_sampled():
     wl, tlen, run = _run(cfg, 512, m)
     mixed = sum(1 for e in run.iterations if (e[:, 0] == 0).any() and (e[:, 0] != 0).any())
     assert mixed > 0
+    ref = run_mixed(wl, 512, m, tlen)
+    assert run.matched == ref["matched"]
+    assert sorted(run.rows) == sorted(ref["rows"])
+    for rid, row in ref["rows"].items():
+        np.testing.assert_array_equal(run.rows[rid], row)
+    print(f"[gpu] batchllm mixed: {len(ref['rows'])} rows bit-exact", flush=True)
     req, pos = run.job_sources()
-    start = _token_starts(run)
     rng = np.random.default_rng(17)
-    picks = rng.choice(len(req), 48, replace=False)
-    # also the first and last token of the job and a decode token of a mixed launch
-    picks = np.concatenate([picks, [0, len(req) - 1]])
+    per_launch = [int(rng.integers(run.iter_off[i], run.iter_off[i + 1])) for i in range(len(run.iterations))]
+    picks = np.unique(np.concatenate([per_launch, rng.choice(len(req), 48, replace=False), [0, len(req) - 1]]))
     reqs = wl.phases[0].requests + wl.phases[1].requests
     by_rid = {r.rid: r for r in reqs}
+    kv_cache = {}
     worst = 0.0
+    o = run.o
     for i in picks:
         r = by_rid[int(run.req_rid[req[i]])]
         p = int(pos[i])
-        k, v = wl.request_full_kv(r)
+        if r.rid not in kv_cache:
+            kv_cache = {r.rid: wl.request_full_kv(r)}
+        k, v = kv_cache[r.rid]
         want = causal_attention(_token_q(wl, r, p)[None], k, v, np.array([p]))[0]
-        got = run.o[int(i)].float().cpu().numpy()
+        got = o[int(i)].float().cpu().numpy()
         worst = max(worst, float(np.abs(got - want).max()))
-    print(f"[gpu] batchllm mixed: {len(run.iterations)} launches ({mixed} mixed), sampled max abs err {worst:.3g}",
-          flush=True)
+    print(f"[gpu] batchllm mixed: {len(run.iterations)} launches ({mixed} mixed), {len(picks)} sampled tokens, "
+          f"max abs err {worst:.3g}", flush=True)
     assert worst <= TOL["bf16"]
-    # indices of sampled requests: each request's row holds its group's
-    # prefix row, then slots no other request holds
-    pre_rows = {int(run.req_rid[g]): run.rows[int(run.req_rid[g])] for g in range(run.G)}
-    assert all(len(row) == run.prefix_len[g] for g, row in enumerate(pre_rows.values()))
-    seen = np.concatenate(list(pre_rows.values()) + [run.rows[int(run.req_rid[run.G + j])][run.prefix_len[g]:]
-                                                     for j, g in enumerate(run.member_group)])
-    assert len(np.unique(seen)) == len(seen) == total

@@ -185,8 +185,29 @@ def test_separate_calls_match_decode_step():
             np.testing.assert_array_equal(x, y)
 
 
+# Sampled leaves at full size: both sides of every kind of tile boundary.
+# Helpdesk: extend tiles of 256 rows (6.4 requests), one 64-row decode tile.
+# BatchLLM / Long-prefix: groups of 16 members (a decode tile each); first
+# and last member of several groups.  Multi-level: 24 leaves under 8
+# branches of 3; decode tiles of 64 rows hold 16 leaves, so leaves 15 and 16
+# sit on either side of a tile boundary inside one branch's sharing.
+FULL_SAMPLES = {
+    "helpdesk": [0, 6, 7, 31, 32, 63],
+    "batchllm": [0, 15, 16, 31, 500, 511, 512, 1008, 1023],
+    "longprefix": [0, 15, 16, 31, 32, 47, 48, 63],
+    "multilevel": [0, 2, 3, 11, 14, 15, 16, 17, 23],
+}
+
+
 @pytest.mark.parametrize("cfg", [c for c in CONFIGS if c.dtype == "bf16"], ids=lambda c: c.name)
 def test_full_size_sampled(cfg):
     """Full-size workloads, default launch configuration (as timed by the
-    benchmark), checked on sampled leaf requests plus the first hint."""
-    run_and_check(cfg, sample_leaves=[0, 1, 17, -1])
+    benchmark), checked on sampled leaf requests, the first hint and, for
+    the multi-level tree, the first, a middle and the last branch request
+    (the middle phase, whose extend attends the root shared by all 8)."""
+    wl = Workload(cfg)
+    extra = []
+    if len(wl.phases) > 2:
+        mid = wl.phases[1].requests
+        extra = [mid[0].rid, mid[len(mid) // 2].rid, mid[-1].rid]
+    run_and_check(cfg, sample_leaves=FULL_SAMPLES[cfg.name], leaf_extra=extra)

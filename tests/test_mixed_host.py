@@ -146,3 +146,27 @@ def test_native_job_under_eviction_matches_the_oracle(pool):
     for rid, row in ref["rows"].items():
         np.testing.assert_array_equal(run.rows[rid], row)
     assert run.rt.tree.stats()["evictions"] == ref["stats"]["evictions"] > 0
+
+
+def test_full_batchllm_job_dry_run_matches_the_oracle():
+    """The full BatchLLM-shaped token-batched job (64 groups x 16, prefix
+    2,000, distinct 200, 1-64 generated tokens; s_chunk 512, M a fifth of
+    the job's K/V entries: the benchmarked job) planned through rdx_job_* on
+    the host: every one of the 1,088 requests' matched length and page-table
+    row equals the oracle's cache run over the oracle's iterations."""
+    from prefix_shared_kv_token_amd.mixed import MixedRun
+    from workloads import config_by_name
+
+    cfg = config_by_name("batchllm")
+    wl = Workload(cfg)
+    tlen = decode_lengths(wl)
+    total = cfg.total_tokens() - (cfg.decode_steps * len(wl.leaf_requests) - int(tlen.sum()))
+    m = 2 * (total // 5)
+    run = MixedRun(wl, 512, m, tlen, device="cpu", stage=False)
+    run.run_native(keep_rows=True, dry_run=True)
+    ref = run_mixed(wl, 512, m, tlen)
+    assert len(ref["rows"]) == 64 + 64 * 16
+    assert run.matched == ref["matched"]
+    assert sorted(run.rows) == sorted(ref["rows"])
+    for rid, row in ref["rows"].items():
+        np.testing.assert_array_equal(run.rows[rid], row)
