@@ -438,7 +438,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="helpdesk")
+    ap.add_argument("--config", default="batchllm",
+                    help="headline workload (default: the largest, BatchLLM micro shape)")
+    ap.add_argument("--also", default="helpdesk,longprefix,multilevel",
+                    help="other workloads measured after the headline (their fractions as extra keys)")
+    ap.add_argument("--also-steps", type=int, default=3)
+    ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--shuffle-seed", type=int, default=None,
                     help="scattered pool: twice the slots, a seeded random half left free before each step")
@@ -477,13 +482,78 @@ def main():
         return
 
     from prefix_shared_kv_token_amd import rdx
-    from prefix_shared_kv_token_amd.driver import WorkloadRun
     from workloads import Workload, config_by_name
 
     cfg = config_by_name(args.config)
     wl = Workload(cfg)
     if args.mixed:
         return run_mixed_bench(args, cfg, wl)
+    m = measure_workload(args, cfg, wl, args.steps, args.warmup, args.instrumented_steps)
+    line = {
+        "metric": "extend query-tokens/s + decode tokens/s; % MFMA peak / % HBM GB/s, 1 MI355X",
+        "value": m["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "instrumented_steps": m["instrumented_steps"],
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1)*sigma Q/K/V, uniform token ids)",
+        "config": m["config"],
+        "extend_query_tokens_per_s": m["extend_query_tokens_per_s"],
+        "decode_tokens_per_s": m["decode_tokens_per_s"],
+        "roofline": m["roofline"],
+        "extend_roofline": m["extend_roofline"],
+        "extend_roofline_hint_plus_member": m["extend_roofline_hint_plus_member"],
+        "hint_extend_roofline": m["hint_extend_roofline"],
+        "decode_roofline": m["decode_roofline"],
+    }
+    if not args.headline_only:
+        # the other bf16 workloads, each from an empty tree with its own
+        # inputs, fewer steps: their kernel fractions beside the headline's
+        others = {}
+        for name in args.also.split(","):
+            if not name or name == cfg.name:
+                continue
+            ocfg = config_by_name(name)
+            print(f"[bench] also {name}", file=sys.stderr, flush=True)
+            om = measure_workload(args, ocfg, Workload(ocfg), args.also_steps, 1, 1)
+            others[name] = {k: om[k] for k in ("value", "ms_per_step", "extend_query_tokens_per_s",
+                                               "decode_tokens_per_s", "extend_roofline",
+                                               "extend_roofline_hint_plus_member", "hint_extend_roofline",
+                                               "decode_roofline")}
+            others[name]["config"] = om["config"]
+            del om
+            import torch
+            torch.cuda.empty_cache()
+        line["workloads"] = others
+    if not args.no_schedule_probe:
+        print("[bench] request ordering on the host tree", file=sys.stderr, flush=True)
+        line["schedule"] = schedule_probe(rdx)
+        line["eviction"] = eviction_probe(rdx)
+        line["prefix_groups"] = prefix_groups_probe(rdx)
+    if not args.no_cpu_baseline:
+        print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        if not args.no_schedule_probe:
+            line["cpu_baseline"]["host_rows"] = cpu_host_rows()
+    print(json.dumps(line, default=float), flush=True)
+
+
+def measure_workload(args, cfg, wl, steps: int, warmup: int, instrumented: int) -> dict:
+    """Times `steps` passes of the whole workload (admission, uploads, KV
+    scatter, extend of every phase, decode steps, finish; empty tree each
+    pass) after `warmup` untimed ones; kernel durations from dispatch-bound
+    HIP events on the last `instrumented` passes."""
+    import numpy as np
+    import torch
+    from prefix_shared_kv_token_amd import rdx
+    from prefix_shared_kv_token_amd.driver import WorkloadRun
+
     print(f"[bench] {cfg.name}: building inputs", file=sys.stderr, flush=True)
     shuffled = args.shuffle_seed is not None
     run = WorkloadRun(wl, extend_items=args.extend_items, decode_items=args.decode_items,
@@ -493,27 +563,27 @@ def main():
     # them would otherwise land inside some step
     gc.collect()
     gc.freeze()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         run.run(keep_outputs=False)
     torch.cuda.synchronize()
     # kernel durations come from HIP events bound to the dispatches of the
-    # last `--instrumented-steps` timed steps (an event-bound dispatch costs
-    # the host extra time, so instrumenting every step would slow the wall
-    # clock the value is computed from)
-    n_inst = max(1, min(args.instrumented_steps, args.steps))
+    # last `instrumented` timed steps (an event-bound dispatch costs the host
+    # extra time, so instrumenting every step would slow the wall clock the
+    # value is computed from)
+    n_inst = max(1, min(instrumented, steps))
     per_run = len(wl.phases) + cfg.decode_steps
     n_launch = n_inst * per_run
-    print(f"[bench] timing {args.steps} steps ({n_inst} instrumented)", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: timing {steps} steps ({n_inst} instrumented)", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i == args.steps - n_inst:
+    for i in range(steps):
+        if i == steps - n_inst:
             rdx.timing_begin(n_launch)
         run.run(keep_outputs=False)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     attn_ms, merge_ms, kinds = rdx.timing_read(n_launch)
     assert len(attn_ms) == n_launch, (len(attn_ms), n_launch)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
 
     # ---- per-launch kernel durations (ms), reshaped [steps, launches/step] ----
     # an attention launch = its attention kernel + the merge kernel behind it
@@ -540,14 +610,27 @@ def main():
         return {"attention_kernel_us": float(a_step[:, cols].mean() * 1e3),
                 "merge_kernel_us": float(m_step[:, cols].mean() * 1e3)}
 
-    ext_tflops = ext_flops / ext_member_s / 1e12
     peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    def mfma_roof(flops, seconds, launches, tokens, cols):
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": peak_tf, "unit": "TFLOP/s", "frac": a / peak_tf,
+                "traffic": None, "avg_launch_us": seconds * 1e6 / launches, **kernel_us(cols),
+                "work_per_launch": f"{flops / launches / 1e9:.2f} GFLOP ({tokens / launches:.0f} query tokens)"}
+
     n_mem = len(member_phases)
-    extend_roof = {"bound": "mfma", "achieved": ext_tflops, "peak": peak_tf, "unit": "TFLOP/s",
-                   "frac": ext_tflops / peak_tf, "traffic": None,
-                   "avg_launch_us": ext_member_s * 1e6 / n_mem, **kernel_us(member_phases),
-                   "work_per_launch": f"{ext_flops / n_mem / 1e9:.2f} GFLOP "
-                                      f"({member_tokens / n_mem:.0f} member query tokens)"}
+    extend_roof = mfma_roof(ext_flops, ext_member_s, n_mem, member_tokens, member_phases)
+    # phase A (the hint prefill: causal attention over the top-level
+    # prefixes, nothing cached) and A+B over every extend launch
+    hint_reqs = wl.phases[0].requests if n_ph > 1 else []
+    all_reqs = [r for ph in wl.phases for r in ph.requests]
+    all_tokens = sum(r.own_len for r in all_reqs)
+    ext_all_s = ext_ms.sum(axis=1).mean() / 1e3
+    ab_roof = mfma_roof(extend_flops(cfg, all_reqs), ext_all_s, n_ph, all_tokens, list(range(n_ph)))
+    hint_roof = None
+    if hint_reqs:
+        hint_s = ext_ms[:, 0].mean() / 1e3
+        hint_roof = mfma_roof(extend_flops(cfg, hint_reqs), hint_s, 1, sum(r.own_len for r in hint_reqs), [0])
     dec_cols = list(range(n_ph, per_step.shape[1]))
     dec_gbs = dec_bytes / dec_total_s / 1e9 if dec_total_s else 0.0
     decode_roof = {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -563,21 +646,10 @@ def main():
             roof["traffic_source"] = t["source"]
     dominant = decode_roof if dec_total_s >= ext_ms.sum(axis=1).mean() / 1e3 else extend_roof
     dominant = dict(dominant, kernel="decode attention" if dominant is decode_roof else "extend attention")
-
-    line = {
-        "metric": "extend query-tokens/s + decode tokens/s; % MFMA peak / % HBM GB/s, 1 MI355X",
+    return {
         "value": tokens_per_step / (ms_per_step / 1e3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "instrumented_steps": n_inst,
-        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic (seeded N(0,1)*sigma Q/K/V, uniform token ids)",
+        "instrumented_steps": n_inst,
         "config": {"workload": cfg.name, "levels": [list(l) for l in cfg.levels],
                    "decode_steps": cfg.decode_steps, "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "tokens_per_step": tokens_per_step, "parallelism": "none (1 GPU)",
@@ -587,19 +659,10 @@ def main():
         "decode_tokens_per_s": cfg.decode_steps * R / dec_total_s if dec_total_s else None,
         "roofline": dominant,
         "extend_roofline": extend_roof,
+        "extend_roofline_hint_plus_member": ab_roof,
+        "hint_extend_roofline": hint_roof,
         "decode_roofline": decode_roof,
     }
-    if not args.no_schedule_probe:
-        print("[bench] request ordering on the host tree", file=sys.stderr, flush=True)
-        line["schedule"] = schedule_probe(rdx)
-        line["eviction"] = eviction_probe(rdx)
-        line["prefix_groups"] = prefix_groups_probe(rdx)
-    if not args.no_cpu_baseline:
-        print("[bench] oracle baseline on host cores", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-        if not args.no_schedule_probe:
-            line["cpu_baseline"]["host_rows"] = cpu_host_rows()
-    print(json.dumps(line, default=float), flush=True)
 
 
 if __name__ == "__main__":
