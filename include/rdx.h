@@ -381,6 +381,24 @@ int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const 
                          const int32_t* page_table, void* o, void* workspace,
                          int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): rdx_decode_attention
+ * with no workspace argument.  The partial states of split tiles go to a
+ * workspace built into the library: one 64 MiB device array per GPU, held
+ * until the process ends (its address is looked up once per device, on the
+ * first call with that device current).  Allocates nothing and calls no
+ * allocating routine.  A plan whose split tiles need more than 64 MiB
+ * (rdx_plan_get_info workspace_bytes) is rejected with EINVAL before
+ * anything is enqueued.  Every call on one GPU uses the same array, and a
+ * call's merge reads what its own attention kernel wrote there: calls that
+ * overlap on one GPU (different streams, no ordering between them) race;
+ * calls on one stream are ordered and safe.  Nothing in the array needs to
+ * start at zero.  Other arguments, results and errors as for
+ * rdx_decode_attention. */
+int rdx_decode_attention_noalloc(const rdx_attn_desc* desc, const rdx_plan* plan, const void* dev_plan,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* page_table, void* o, void* stream);
+
 /* ------------------------------------------------------- decode step */
 /* Caller-owned device buffers of one step. */
 typedef struct rdx_step_io {

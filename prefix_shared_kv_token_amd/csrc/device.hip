@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "attn_kernels.h"
@@ -18,7 +19,37 @@
 
 using namespace rdx;
 
+// Device-resident workspace of rdx_decode_attention_noalloc: the partial
+// (o, max, sum) states of split tiles.  One copy per GPU, held until the
+// process ends.  Host code never passes this name to a kernel (in host code
+// it is a stand-in, not a device address): it uses the per-device address
+// from hipGetSymbolAddress instead.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of `scratch` on the current device, looked up once per device
+// with that device current (the first call on the device).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RDX_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RDX_EUNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(RDX_EDEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
 
 // Launch timing state (see rdx_timing_begin): per launch one event pair
 // bound to the attention dispatch and, for plans with split tiles, one bound
@@ -33,11 +64,12 @@ struct Timing {
 
 // Launches the attention kernel and, for plans with split tiles, the merge
 // kernel behind it; while timing is on, each dispatch carries its own events.
+// untimed: never record (the no-allocation entry point creates no events)
 template <typename KA, typename KM>
 hipError_t launch(KA attn, KM merge, int64_t n_items, int64_t n_merge, hipStream_t st, int32_t kind,
-                  const AttnArgs& a, int threads = kThreads) {
+                  const AttnArgs& a, int threads = kThreads, bool untimed = false) {
   hipEvent_t* ev = nullptr;
-  if (g_timing.on && g_timing.used < g_timing.cap) {
+  if (!untimed && g_timing.on && g_timing.used < g_timing.cap) {
     const int32_t i = g_timing.used;
     while ((int32_t)g_timing.kind.size() <= i) {
       for (int k = 0; k < 4; ++k) {
@@ -77,7 +109,7 @@ bool same_shape(const rdx_attn_desc& a, const rdx_attn_desc& b) {
 
 int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t kind, const void* dev_plan,
                      const void* q, const void* kp, const void* vp, const int32_t* pt, void* o, void* ws,
-                     int64_t ws_bytes, void* stream) {
+                     int64_t ws_bytes, void* stream, bool untimed = false) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!hplan) return fail(RDX_EINVAL, "attention: null plan");
@@ -129,27 +161,27 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   const bool off32 = a.pool_bytes < ((int64_t)1 << 31);
   if (desc->dtype == RDX_BF16 && p->tile_rows == kDecodeTileRows) {
     if (desc->head_dim == 128)
-      e = off32 ? launch(attn_decode_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a)
-                : launch(attn_decode_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a);
+      e = off32 ? launch(attn_decode_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a, kThreads, untimed)
+                : launch(attn_decode_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a, kThreads, untimed);
     else
-      e = off32 ? launch(attn_decode_kernel<64, true>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a)
-                : launch(attn_decode_kernel<64, false>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a);
+      e = off32 ? launch(attn_decode_kernel<64, true>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a, kThreads, untimed)
+                : launch(attn_decode_kernel<64, false>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a, kThreads, untimed);
   } else if (desc->dtype == RDX_BF16 && p->tile_rows == 256) {
     e = off32 ? launch(attn_bf16_wide_kernel<true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a,
-                       kWideThreads)
+                       kWideThreads, untimed)
               : launch(attn_bf16_wide_kernel<false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a,
-                       kWideThreads);
+                       kWideThreads, untimed);
   } else if (desc->dtype == RDX_BF16) {
     if (desc->head_dim == 128)
-      e = off32 ? launch(attn_bf16_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a)
-                : launch(attn_bf16_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a);
+      e = off32 ? launch(attn_bf16_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a, kThreads, untimed)
+                : launch(attn_bf16_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a, kThreads, untimed);
     else
-      e = off32 ? launch(attn_bf16_kernel<64, true>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a)
-                : launch(attn_bf16_kernel<64, false>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a);
+      e = off32 ? launch(attn_bf16_kernel<64, true>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a, kThreads, untimed)
+                : launch(attn_bf16_kernel<64, false>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a, kThreads, untimed);
   }
   else
-    e = desc->head_dim == 128 ? launch(attn_f32_kernel<128>, merge_kernel<float, 128>, n_items, n_merge, st, kind, a)
-                              : launch(attn_f32_kernel<64>, merge_kernel<float, 64>, n_items, n_merge, st, kind, a);
+    e = desc->head_dim == 128 ? launch(attn_f32_kernel<128>, merge_kernel<float, 128>, n_items, n_merge, st, kind, a, kThreads, untimed)
+                              : launch(attn_f32_kernel<64>, merge_kernel<float, 64>, n_items, n_merge, st, kind, a, kThreads, untimed);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -303,6 +335,23 @@ int rdx_decode_attention(const rdx_attn_desc* desc, const rdx_plan* plan, const 
                          int64_t workspace_bytes, void* stream) {
   return launch_attention(desc, plan, RDX_PLAN_DECODE, dev_plan, q, k_pool, v_pool, page_table, o, workspace,
                           workspace_bytes, stream);
+}
+
+int rdx_decode_attention_noalloc(const rdx_attn_desc* desc, const rdx_plan* plan, const void* dev_plan,
+                                 const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                                 void* o, void* stream) {
+  if (!plan) return fail(RDX_EINVAL, "rdx_decode_attention_noalloc: null plan");
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  if (p->ws_bytes > kNoAllocScratchBytes)
+    return fail(RDX_EINVAL, "rdx_decode_attention_noalloc: the plan's split tiles need %lld bytes of workspace, "
+                "the built-in workspace holds %lld", (long long)p->ws_bytes, (long long)kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (p->ws_bytes > 0) {
+    int rc = scratch_address(&ws);
+    if (rc) return rc;
+  }
+  return launch_attention(desc, plan, RDX_PLAN_DECODE, dev_plan, q, k_pool, v_pool, page_table, o, ws,
+                          p->ws_bytes > 0 ? kNoAllocScratchBytes : 0, stream, /*untimed=*/true);
 }
 
 // The device tail of a step whose plan is built: the work list staged in

@@ -111,6 +111,7 @@ _SIGS = {
     "rdx_plan_upload": (ctypes.c_int, [vp, vp, i64, vp, i64, vp]),
     "rdx_extend_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
     "rdx_decode_attention": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+    "rdx_decode_attention_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp]),
     "rdx_decode_step": (ctypes.c_int, [vp, vp, ctypes.POINTER(AttnDesc), i32, i64p, i32p, i32p, i32p, i32p, i64,
                                        i64, i32p, ctypes.POINTER(StepIO), vp, ctypes.POINTER(PlanInfo)]),
     "rdx_timing_begin": (ctypes.c_int, [i32]),
@@ -461,6 +462,12 @@ def decode_attention(desc: AttnDesc, plan: Plan, dev_plan, q, k_pool, v_pool, pa
     _check(lib().rdx_decode_attention(ctypes.byref(desc), plan.handle, _ptr(dev_plan), _ptr(q), _ptr(k_pool),
                                       _ptr(v_pool), _ptr(page_table), _ptr(o), _ptr(workspace),
                                       workspace_bytes, _stream(stream)))
+
+
+def decode_attention_noalloc(desc: AttnDesc, plan: Plan, dev_plan, q, k_pool, v_pool, page_table, o, stream=None):
+    _check(lib().rdx_decode_attention_noalloc(ctypes.byref(desc), plan.handle, _ptr(dev_plan), _ptr(q),
+                                              _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(o),
+                                              _stream(stream)))
 
 
 def timing_begin(cap: int):

@@ -33,6 +33,11 @@ int rdx_decode_attention(const rdx_attn_desc*, const rdx_plan*, const void*, con
   return no_device("rdx_decode_attention");
 }
 
+int rdx_decode_attention_noalloc(const rdx_attn_desc*, const rdx_plan*, const void*, const void*, const void*,
+                                 const void*, const int32_t*, void*, void*) {
+  return no_device("rdx_decode_attention_noalloc");
+}
+
 int rdx_decode_step(rdx_tree*, rdx_plan*, const rdx_attn_desc*, int32_t, const int64_t*, const int32_t*, int32_t*,
                     int32_t*, int32_t*, int64_t, int64_t, int32_t*, const rdx_step_io*, void*, rdx_plan_info*) {
   return no_device("rdx_decode_step");
