@@ -105,6 +105,10 @@ EDGE = [
     ("tiny", dict(levels=((1, 40), (3, 17), (2, 9)), n_q_heads=8, n_kv_heads=2, head_dim=128, decode_steps=6)),
     # GQA 8 (group of 8 query heads per KV head)
     ("longprefix", dict(levels=((2, 300), (4, 33)), n_q_heads=16, n_kv_heads=2, decode_steps=3)),
+    # 24 leaves x 4 grouped heads = 96 decode rows under one root: one
+    # decode tile of two 16-row groups per wave (head_dim 128 and 64)
+    ("multilevel", dict(levels=((1, 100), (2, 40), (12, 11)), decode_steps=4)),
+    ("tiny", dict(levels=((1, 90), (24, 13)), n_q_heads=8, n_kv_heads=2, dtype="bf16", sigma=0.5, decode_steps=3)),
 ]
 
 
