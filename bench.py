@@ -189,15 +189,15 @@ def kernel_source_digest() -> str:
 
 
 def measured_traffic(kind: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary
-    (profiles/<kind>_attention_<workload>_traffic.md), or None when there is
-    none or it was taken from different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{kind}_attention_{workload}_traffic.md")
+    """HBM bytes per launch (kind: "decode" or "extend member") from the
+    committed rocprofv3 counter summary profiles/traffic_<workload>.md, or
+    None when there is none or it was taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
-    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch\[" + re.escape(kind) + r"\]:\s*([0-9]+)", text)
     if not m_src or not m_val or m_src.group(1) != kernel_source_digest():
         return None
     return {"bytes_per_launch": int(m_val.group(1)), "source": os.path.relpath(path, ROOT)}
@@ -639,7 +639,7 @@ def measure_workload(args, cfg, wl, steps: int, warmup: int, instrumented: int) 
                    **(kernel_us(dec_cols) if dec_cols else {}),
                    "work_per_launch": f"{dec_bytes / max(1, cfg.decode_steps) / 1e6:.1f} MB (mean over "
                                       f"{cfg.decode_steps} decode steps)"}
-    for kname, roof in (("extend", extend_roof), ("decode", decode_roof)):
+    for kname, roof in (("extend member", extend_roof), ("decode", decode_roof)):
         t = measured_traffic(kname, cfg.name)
         if t is not None:
             roof["traffic"] = t["bytes_per_launch"]

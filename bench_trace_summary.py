@@ -1,0 +1,129 @@
+#!/usr/bin/env python3
+"""Summarises rocprofv3 output of `bench.py --headline-only` runs into the
+tables kept under profiles/: kernel durations (from --kernel-trace) and, given
+the two counter passes, HBM bytes per dispatch (FETCH_SIZE and WRITE_SIZE,
+each scaled by the factor a plain device copy of known size gives).
+
+Dispatches are classified by kernel and position: a bench step launches the
+extend attention of every phase in order (phase 0 = the hint prefill of the
+top-level prefixes, then the member phases), each followed by its merge
+kernel when the plan split tiles, then one decode attention (+ merge) per
+decode step.  So the k-th extend dispatch of the run belongs to phase
+k mod n_phases, and a merge kernel belongs to the attention dispatch right
+before it.
+
+    python3 bench_trace_summary.py trace <run_kernel_trace.csv> --phases N
+    python3 bench_trace_summary.py pmc <FETCH run_counter_collection.csv> <WRITE ...csv> --phases N \\
+        --fetch-factor F --write-factor W
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+
+EXTEND = ("attn_bf16_wide_kernel", "attn_bf16_kernel", "attn_f32_kernel")
+
+
+def _rows(path):
+    rows = list(csv.DictReader(open(path)))
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else "Correlation_Id"
+    rows.sort(key=lambda r: int(r[key]))
+    return rows
+
+
+def _short(name: str) -> str:
+    for k in ("attn_decode_kernel", "merge_kernel") + EXTEND:
+        if k in name:
+            i = name.index(k)
+            j = name.find("(", i)
+            return name[i:j if j > 0 else None]
+    return name.split("(")[0][:60]
+
+
+def classify(names, n_phases: int):
+    """-> class label per dispatch (same order)."""
+    out, n_ext, last = [], 0, None
+    for name in names:
+        if any(k in name for k in EXTEND):
+            ph = n_ext % n_phases
+            n_ext += 1
+            role = "hint" if (ph == 0 and n_phases > 1) else "member"
+            last = f"extend phase {ph} ({role})"
+            out.append(f"{last}: {_short(name)}")
+        elif "attn_decode_kernel" in name:
+            last = "decode"
+            out.append(f"decode: {_short(name)}")
+        elif "merge_kernel" in name:
+            out.append(f"merge after {last}")
+        else:
+            out.append(_short(name))
+    return out
+
+
+def trace(path, n_phases):
+    rows = _rows(path)
+    labels = classify([r["Kernel_Name"] for r in rows], n_phases)
+    dur = collections.defaultdict(list)
+    for r, lab in zip(rows, labels):
+        dur[lab].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    tot = sum(sum(v) for v in dur.values())
+    print("| dispatch class | calls | average (us) | total (ms) | share |")
+    print("|---|---:|---:|---:|---:|")
+    for lab, v in sorted(dur.items(), key=lambda x: -sum(x[1])):
+        print(f"| `{lab}` | {len(v)} | {sum(v) / len(v):.2f} | {sum(v) / 1e3:.2f} | {100 * sum(v) / tot:.1f}% |")
+
+
+def pmc(fetch_path, write_path, n_phases, ff, wf):
+    res = {}
+    for which, path in (("fetch", fetch_path), ("write", write_path)):
+        rows = _rows(path)
+        labels = classify([r["Kernel_Name"] for r in rows], n_phases)
+        acc = collections.defaultdict(list)
+        for r, lab in zip(rows, labels):
+            acc[lab].append(float(r["Counter_Value"]))
+        res[which] = acc
+    print("| dispatch class | dispatches | FETCH_SIZE mean KiB | WRITE_SIZE mean KiB | scaled MB/dispatch |")
+    print("|---|---:|---:|---:|---:|")
+    scaled = {}
+    for lab in sorted(res["fetch"], key=lambda k: -sum(res["fetch"][k])):
+        f = res["fetch"][lab]
+        w = res["write"].get(lab, [0.0])
+        fm, wm = sum(f) / len(f), sum(w) / len(w)
+        scaled[lab] = (fm * ff + wm * wf) * 1024
+        print(f"| `{lab}` | {len(f)} | {fm:,.1f} | {wm:,.1f} | {scaled[lab] / 1e6:,.2f} |")
+    # per launch: an attention dispatch plus the merge behind it
+    dec = [k for k in scaled if k.startswith("decode: ")]
+    if dec:
+        b = scaled[dec[0]] + scaled.get("merge after decode", 0.0)
+        print(f"\ntraffic_bytes_per_launch[decode]: {b:.0f}")
+    mem = sorted({k.split(":")[0] for k in scaled if k.startswith("extend phase") and "(member)" in k})
+    if mem:
+        per = []
+        for ph in mem:
+            att = [v for k, v in scaled.items() if k.startswith(ph + ":")][0]
+            per.append(att + scaled.get(f"merge after {ph}", 0.0))
+        print(f"traffic_bytes_per_launch[extend member]: {sum(per) / len(per):.0f}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("csv")
+    t.add_argument("--phases", type=int, required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("fetch_csv")
+    p.add_argument("write_csv")
+    p.add_argument("--phases", type=int, required=True)
+    p.add_argument("--fetch-factor", type=float, required=True)
+    p.add_argument("--write-factor", type=float, required=True)
+    a = ap.parse_args()
+    if a.cmd == "trace":
+        trace(a.csv, a.phases)
+    else:
+        pmc(a.fetch_csv, a.write_csv, a.phases, a.fetch_factor, a.write_factor)
+
+
+if __name__ == "__main__":
+    main()

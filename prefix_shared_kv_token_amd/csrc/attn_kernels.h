@@ -730,70 +730,61 @@ __device__ __forceinline__ void dec_store(DecTile<D>& t, const DecStage<CPT>& st
   }
 }
 
-// One 64-key block for one wave's RG groups of 16 rows (lane: row rr = lane
-// % 16 of each group, lane group g = lane / 16).  rel[r]: block-local keys <
-// rel[r] are visible to the lane's row of group r.  Each K and V^T fragment
-// read from LDS feeds the MFMAs of all RG groups.
-template <int D, int RG>
-__device__ __forceinline__ void dec_block(const DecTile<D>& t, const bf16x8 (&qf)[RG][D / 32],
-                                          f32x4 (&acc)[RG][D / 16], float (&m_run)[RG], float (&l_run)[RG],
-                                          const int (&rel)[RG], float c2, int rr, int g) {
+// One 64-key block for one wave's 16 rows (lane: row rr = lane % 16, lane
+// group g = lane / 16).  rel: block-local keys < rel are visible to the row.
+template <int D>
+__device__ __forceinline__ void dec_block(const DecTile<D>& t, const bf16x8 (&qf)[D / 32], f32x4 (&acc)[D / 16],
+                                          float& m_run, float& l_run, int rel, float c2, int rr, int g) {
   constexpr int KS = DecTile<D>::KS, VS = DecTile<D>::VS;
   constexpr int DB = D / 32, DT = D / 16;
-  f32x4 s[RG][4];
+  f32x4 s[4];
 #pragma unroll
-  for (int r = 0; r < RG; ++r)
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) s[r][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&t.k[(16 * kt + rr) * KS + 32 * db + 8 * g]);
-#pragma unroll
-      for (int r = 0; r < RG; ++r) s[r][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[r][db], s[r][kt], 0, 0, 0);
+      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[db], s[kt], 0, 0, 0);
     }
-  bf16x8 pk[RG][2];
+  if (__ballot(rel < 64)) {
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    if (__ballot(rel[r] < 64)) {
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[r][kt][e] = 16 * kt + 4 * g + e < rel[r] ? s[r][kt][e] : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(fmaxf(s[r][0][0], s[r][0][1]), fmaxf(s[r][0][2], s[r][0][3])),
-                     fmaxf(fmaxf(s[r][1][0], s[r][1][1]), fmaxf(s[r][1][2], s[r][1][3])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[r][2][0], s[r][2][1]), fmaxf(s[r][2][2], s[r][2][3])),
-                         fmaxf(fmaxf(s[r][3][0], s[r][3][1]), fmaxf(s[r][3][2], s[r][3][3]))));
-    mx = half_swap_max(row16_swap_max(mx));
-    // lazy rescale (see wave_block)
-    const float t_max = mx * c2;
-    const float m_new = t_max > m_run[r] + 8.f ? t_max : m_run[r];
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run[r] - m_use);
-    float lsp[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[r][kt][e] = exp2_fast(fmaf(s[r][kt][e], c2, -m_use));
-      lsp[kt] = (s[r][kt][0] + s[r][kt][1]) + (s[r][kt][2] + s[r][kt][3]);
-    }
-    // per-lane partial sum over this lane's keys (lanes of a row share m)
-    l_run[r] = l_run[r] * alpha + ((lsp[0] + lsp[1]) + (lsp[2] + lsp[3]));
-    m_run[r] = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[r][dt] *= alpha;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pk[r][h][e] = (__bf16)s[r][2 * h][e];
-        pk[r][h][4 + e] = (__bf16)s[r][2 * h + 1][e];
-      }
+      for (int r = 0; r < 4; ++r) s[kt][r] = 16 * kt + 4 * g + r < rel ? s[kt][r] : -INFINITY;
   }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+  mx = half_swap_max(row16_swap_max(mx));
+  // lazy rescale (see wave_block)
+  const float t_max = mx * c2;
+  const float m_new = t_max > m_run + 8.f ? t_max : m_run;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2_fast(m_run - m_use);
+  float lsp[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[kt][r] = exp2_fast(fmaf(s[kt][r], c2, -m_use));
+    lsp[kt] = (s[kt][0] + s[kt][1]) + (s[kt][2] + s[kt][3]);
+  }
+  // per-lane partial sum over this lane's keys (lanes of a row share m)
+  l_run = l_run * alpha + ((lsp[0] + lsp[1]) + (lsp[2] + lsp[3]));
+  m_run = m_new;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+  }
+  bf16x8 pk[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pk[h][r] = (__bf16)s[2 * h][r];
+      pk[h][4 + r] = (__bf16)s[2 * h + 1][r];
+    }
   // O^T += V^T P^T: lane (rr, g) reads 8 bytes of V row 32h + 4g + rr/4 (and
   // +16) at column 16 dt + 4 (rr % 4); the transposing read hands it the
   // column rr of that 16 x 4 patch
@@ -809,15 +800,11 @@ __device__ __forceinline__ void dec_block(const DecTile<D>& t, const bf16x8 (&qf
       // read's result is not lowered correctly by this compiler)
       const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
       const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lw.x, lw.y, hw.x, hw.y});
-#pragma unroll
-      for (int r = 0; r < RG; ++r) acc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[r][h], acc[r][dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[h], acc[dt], 0, 0, 0);
     }
 }
 
-// RG: 16-row groups per wave; a tile holds up to 64 RG rows (RG = 2 for
-// sharing groups of 65..128 decode rows, so one workgroup streams the shared
-// keys once for all of them).
-template <int D, bool OFF32, int RG>
+template <int D, bool OFF32>
 __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   __shared__ DecTile<D> buf[2];
   constexpr int DB = D / 32, DT = D / 16;
@@ -836,44 +823,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   const int act_lo = item[8], act_hi = item[9], ws_base = item[10];
   const int group = a.group;
   const int n_rows = n_tok * group;
-  // wave w owns rows 16 RG w .. 16 RG w + 16 RG - 1; group r of them starts at 16 (RG w + r)
-  int row[RG], tloc[RG], qpos[RG];
-  bool row_ok[RG];
-  bool wave_live = false;
-#pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    row[r] = 16 * (RG * wave + r) + rr;
-    tloc[r] = row[r] / group;
-    row_ok[r] = row[r] < n_rows && tloc[r] >= act_lo && tloc[r] < act_hi;
-    wave_live = wave_live || __ballot(row_ok[r]) != 0;
-  }
+  const int row = 16 * wave + rr;
+  const int tloc = row / group;
+  const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
+  const bool wave_live = __ballot(row_ok) != 0;
 
   // Q (B operand of S^T): Q[row][32 db + 8 g .. +8)
-  bf16x8 qf[RG][DB];
+  bf16x8 qf[DB];
+  int qpos = 0;
+  if (row_ok) {
+    const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
+    qpos = tk[1];
+    const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
+                        ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * g;
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    qpos[r] = 0;
-    if (row_ok[r]) {
-      const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc[r]) * kTokWords;
-      qpos[r] = tk[1];
-      const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
-                          ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row[r] % group) * D + 8 * g;
+    for (int db = 0; db < DB; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(src + 32 * db);
+  } else {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) qf[r][db] = *reinterpret_cast<const bf16x8*>(src + 32 * db);
-    } else {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) qf[r][db] = bf16x8{};
-    }
+    for (int db = 0; db < DB; ++db) qf[db] = bf16x8{};
   }
-  f32x4 acc[RG][DT];
-  float m_run[RG], l_run[RG];
+  f32x4 acc[DT];
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
   const float c2 = a.scale_log2;
 
   DecPool<D, OFF32> pool;
@@ -882,17 +854,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   const uint32_t in_row = (uint32_t)(kvh * D + 8 * CPT * cq) * 2;
   // slot of this thread's key in the block the iterator is at (-1: none)
   auto slot_of = [&](const BlockIter& it) { return it.kb + kk < it.k1 ? it.prow[it.kb + kk] : -1; };
-  // the visible-key limit of each row group for a job
-  int lim[RG];
-  auto view = [&](int k1, int lo, int hi_t, int causal, int k0) {
-    bool any = false;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      lim[r] = (row_ok[r] && tloc[r] >= lo && tloc[r] < hi_t) ? (causal ? min(k1, qpos[r] + 1) : k1) : 0;
-      any = any || __ballot(lim[r] > k0) != 0;
-    }
-    return wave_live && any;
-  };
 
   if (nblk > 0) {
     BlockIter it_s, it_c;
@@ -915,7 +876,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
 
     // the first job's view from the item record
     int cur_job = jb;
-    bool wave_job = view(item[13], item[14], item[15], item[16], item[12]);
+    int lim = (row_ok && tloc >= item[14] && tloc < item[15]) ? (item[16] ? min(item[13], qpos + 1) : item[13]) : 0;
+    bool wave_job = wave_live && __ballot(lim > item[12]) != 0;
     // block b: compute from buf[b & 1]; the registers of block b+1 are
     // stored behind it; block b+2 is issued into the registers block b used
     // Issue order matters (loads retire in order for the wait counter): the
@@ -929,14 +891,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
       if (it_c.j != cur_job) {
         cur_job = it_c.j;
         const int32_t* job = a.jobs + (int64_t)cur_job * kJobWords;
-        wave_job = view(job[2], job[3], job[4], job[5], job[1]);
+        const int k1 = job[2], lo = job[3], hi_t = job[4], causal = job[5];
+        lim = (row_ok && tloc >= lo && tloc < hi_t) ? (causal ? min(k1, qpos + 1) : k1) : 0;
+        wave_job = wave_live && __ballot(lim > job[1]) != 0;
       }
-      if (wave_job && b < nblk) {
-        int rel[RG];
-#pragma unroll
-        for (int r = 0; r < RG; ++r) rel[r] = lim[r] - it_c.kb;
-        dec_block<D, RG>(buf[b & 1], qf, acc, m_run, l_run, rel, c2, rr, g);
-      }
+      if (wave_job && b < nblk) dec_block<D>(buf[b & 1], qf, acc, m_run, l_run, lim - it_c.kb, c2, rr, g);
       dec_store<D, CPT>(buf[(b + 1) & 1], next, kk, cq);
       iter_next(a, it_c, je);
       __syncthreads();
@@ -950,33 +909,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   }
 
   // ---- result: rows of this lane (4 lane groups share a row) ----
-#pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const float l_tot = half_swap_sum(row16_swap_sum(l_run[r]));
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (!row_ok[r]) continue;  // row_ok implies act_lo <= tloc < act_hi
-    if (!split) {
-      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc[r]) * kTokWords];
-      __bf16* dst = reinterpret_cast<__bf16*>(a.o) +
-                    ((int64_t)q_index * a.hq + (int64_t)kvh * group + row[r] % group) * D;
+  const float l_tot = half_swap_sum(row16_swap_sum(l_run));
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!split) {
+    if (row_ok) {
+      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
+      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[r][dt][e] * inv);
+        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[dt][r] * inv);
         *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * g) = v;
       }
-    } else {
-      const int64_t w = ((int64_t)kvh * a.ws_tokens + ws_base + tloc[r] - act_lo) * group + row[r] % group;
-      float* dst = a.ws_o + w * D;
+    }
+    return;
+  }
+  if (row_ok) {  // row_ok implies act_lo <= tloc < act_hi
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + ws_base + tloc - act_lo) * group + row % group;
+    float* dst = a.ws_o + w * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) =
-            make_float4(acc[r][dt][0] * inv, acc[r][dt][1] * inv, acc[r][dt][2] * inv, acc[r][dt][3] * inv);
-      if (g == 0) {
-        a.ws_ml[w * 2] = m_run[r];
-        a.ws_ml[w * 2 + 1] = l_tot;
-      }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) =
+          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+    if (g == 0) {
+      a.ws_ml[w * 2] = m_run;
+      a.ws_ml[w * 2 + 1] = l_tot;
     }
   }
 }

@@ -197,13 +197,10 @@ int rdx_plan_create(const rdx_attn_desc* desc, int32_t kind, int32_t target_item
   p->kind = kind;
   p->target_items = target_items;
   if (kind == RDX_PLAN_EXTEND && desc->dtype == RDX_BF16 && desc->head_dim == 128) p->tile_rows = 2 * rdx::kTileRows;
-  // bf16 decode: tiles of up to 128 rows for the decode kernel, so a
-  // sharing group's new tokens x the GQA group (e.g. 24 requests x 4 heads)
-  // stream the group's shared keys in one tile
-  if (kind == RDX_PLAN_DECODE && desc->dtype == RDX_BF16) {
+  // bf16 decode: 64-row tiles for the decode kernel (a group's new tokens x
+  // the GQA group fit one tile whenever the group has at most 64 heads)
+  if (kind == RDX_PLAN_DECODE && desc->dtype == RDX_BF16 && desc->num_q_heads / desc->num_kv_heads <= 64)
     p->tile_rows = rdx::kDecodeTileRows;
-    p->decode_kernel = true;
-  }
   *out = reinterpret_cast<rdx_plan*>(p);
   return rdx::ok();
 }

@@ -159,22 +159,13 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   // pools under 2 GiB are addressed with 32-bit buffer offsets (the buffer
   // resource's record count is a signed 32-bit value here)
   const bool off32 = a.pool_bytes < ((int64_t)1 << 31);
-  if (desc->dtype == RDX_BF16 && p->decode_kernel) {
-    // one 16-row group per wave while every tile has at most 64 rows, two
-    // beyond (each staged K/V block then feeds up to 128 rows)
-    const bool wide = p->max_tile_rows > 64;
-    auto dec = [&](auto kern) {
-      return launch(kern, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a, kThreads, untimed);
-    };
-    auto dec64 = [&](auto kern) {
-      return launch(kern, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a, kThreads, untimed);
-    };
+  if (desc->dtype == RDX_BF16 && p->tile_rows == kDecodeTileRows) {
     if (desc->head_dim == 128)
-      e = off32 ? (wide ? dec(attn_decode_kernel<128, true, 2>) : dec(attn_decode_kernel<128, true, 1>))
-                : (wide ? dec(attn_decode_kernel<128, false, 2>) : dec(attn_decode_kernel<128, false, 1>));
+      e = off32 ? launch(attn_decode_kernel<128, true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a, kThreads, untimed)
+                : launch(attn_decode_kernel<128, false>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a, kThreads, untimed);
     else
-      e = off32 ? (wide ? dec64(attn_decode_kernel<64, true, 2>) : dec64(attn_decode_kernel<64, true, 1>))
-                : (wide ? dec64(attn_decode_kernel<64, false, 2>) : dec64(attn_decode_kernel<64, false, 1>));
+      e = off32 ? launch(attn_decode_kernel<64, true>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a, kThreads, untimed)
+                : launch(attn_decode_kernel<64, false>, merge_kernel<__bf16, 64>, n_items, n_merge, st, kind, a, kThreads, untimed);
   } else if (desc->dtype == RDX_BF16 && p->tile_rows == 256) {
     e = off32 ? launch(attn_bf16_wide_kernel<true>, merge_kernel<__bf16, 128>, n_items, n_merge, st, kind, a,
                        kWideThreads, untimed)

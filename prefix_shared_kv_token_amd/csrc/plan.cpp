@@ -234,8 +234,6 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   }
   const int ntiles = (int)sc.tile_tr_begin.size();
   sc.tile_tr_begin.push_back((int)sc.trs.size());
-  max_tile_rows = 0;
-  for (int t = 0; t < ntiles; ++t) max_tile_rows = std::max(max_tile_rows, tiles[t * kTileWords + 1] * group());
 
   // ---- jobs per tile (before splitting): its shared segments, then each
   // request's own causal range ----

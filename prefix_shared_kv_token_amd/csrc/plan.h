@@ -18,7 +18,7 @@ namespace rdx {
 
 constexpr int kTileRows = 128;   // query rows (token x grouped head) per tile
 constexpr int kKeyBlock = 64;    // keys per inner iteration of the kernels
-constexpr int kDecodeTileRows = 128;  // query rows per tile of the bf16 decode kernel (64 per row-group variant)
+constexpr int kDecodeTileRows = 64;  // query rows per tile of the bf16 decode kernel
 
 // Record layouts (int32 words) -- shared with the device code.
 // item: one per key chunk, run for every KV head.  Words 0-3: tile,
@@ -51,8 +51,6 @@ struct Plan {
   // the tile fields the merge needs (kMBlockWords)
   std::vector<int32_t> items, tiles, jobs, toks, contribs, runs, run_slots, new_slots, cptr, clist, mblocks;
   int64_t num_split_tiles = 0, num_shared_segments = 0, ws_tokens = 0, key_rows = 0;
-  int32_t max_tile_rows = 0;  // the most query rows of any tile
-  bool decode_kernel = false;  // launched on the bf16 decode kernel
   int64_t max_page_row = -1;
   // device blob layout, in int32 words
   int64_t off_items = 0, off_tiles = 0, off_jobs = 0, off_toks = 0, off_contribs = 0,
@@ -75,8 +73,7 @@ struct Plan {
   std::vector<void*> retired;  // outgrown staging buffers, freed with the plan
 
   // query rows per tile: 256 for the wide bf16 head_dim-128 extend kernel,
-  // kDecodeTileRows for the bf16 decode kernel, kTileRows otherwise (the
-  // fp32 kernel and the 4-wave bf16 extend kernel)
+  // kDecodeTileRows for the bf16 decode kernel, kTileRows otherwise
   int tile_rows = kTileRows;
   int group() const { return desc.num_q_heads / desc.num_kv_heads; }
   int tile_tokens() const { return tile_rows / group(); }
