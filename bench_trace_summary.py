@@ -12,7 +12,7 @@ decode step.  So the k-th extend dispatch of the run belongs to phase
 k mod n_phases, and a merge kernel belongs to the attention dispatch right
 before it.
 
-    python3 bench_trace_summary.py trace <run_kernel_trace.csv> --phases N
+    python3 bench_trace_summary.py trace <run_kernel_trace.csv> --phases N --runs R
     python3 bench_trace_summary.py pmc <FETCH run_counter_collection.csv> <WRITE ...csv> --phases N \\
         --fetch-factor F --write-factor W
 """
@@ -61,17 +61,22 @@ def classify(names, n_phases: int):
     return out
 
 
-def trace(path, n_phases):
+def trace(path, n_phases, runs):
+    """runs: passes of the workload in the traced run (warm-up + timed); the
+    last column averages the dispatches of the last pass only, the one whose
+    kernels bench.py times with events."""
     rows = _rows(path)
     labels = classify([r["Kernel_Name"] for r in rows], n_phases)
     dur = collections.defaultdict(list)
     for r, lab in zip(rows, labels):
         dur[lab].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     tot = sum(sum(v) for v in dur.values())
-    print("| dispatch class | calls | average (us) | total (ms) | share |")
-    print("|---|---:|---:|---:|---:|")
+    print("| dispatch class | calls | average (us) | total (ms) | share | average, last pass (us) |")
+    print("|---|---:|---:|---:|---:|---:|")
     for lab, v in sorted(dur.items(), key=lambda x: -sum(x[1])):
-        print(f"| `{lab}` | {len(v)} | {sum(v) / len(v):.2f} | {sum(v) / 1e3:.2f} | {100 * sum(v) / tot:.1f}% |")
+        last = v[-(len(v) // runs):] if runs and len(v) % runs == 0 and len(v) >= runs else None
+        tail = f"{sum(last) / len(last):.2f}" if last else "-"
+        print(f"| `{lab}` | {len(v)} | {sum(v) / len(v):.2f} | {sum(v) / 1e3:.2f} | {100 * sum(v) / tot:.1f}% | {tail} |")
 
 
 def pmc(fetch_path, write_path, n_phases, ff, wf):
@@ -112,6 +117,7 @@ def main():
     t = sub.add_parser("trace")
     t.add_argument("csv")
     t.add_argument("--phases", type=int, required=True)
+    t.add_argument("--runs", type=int, default=0, help="workload passes in the run (warm-up + timed)")
     p = sub.add_parser("pmc")
     p.add_argument("fetch_csv")
     p.add_argument("write_csv")
@@ -120,7 +126,7 @@ def main():
     p.add_argument("--write-factor", type=float, required=True)
     a = ap.parse_args()
     if a.cmd == "trace":
-        trace(a.csv, a.phases)
+        trace(a.csv, a.phases, a.runs)
     else:
         pmc(a.fetch_csv, a.write_csv, a.phases, a.fetch_factor, a.write_factor)
 
