@@ -46,6 +46,7 @@ struct Req {
 
 struct TileReq {
   int r, lo, hi;  // request, its tile-local token range
+  int32_t pmax;   // the position of its last token in the tile
 };
 
 struct Job {
@@ -225,8 +226,9 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
       }
       int32_t* tl = &tiles[(ntile - 1) * kTileWords];
       int local = tl[1];
-      if ((int)sc.trs.size() == sc.tile_tr_begin.back() || sc.trs.back().r != r) sc.trs.push_back({r, local, local});
+      if ((int)sc.trs.size() == sc.tile_tr_begin.back() || sc.trs.back().r != r) sc.trs.push_back({r, local, local, 0});
       sc.trs.back().hi = local + 1;
+      sc.trs.back().pmax = q.kv_len - q.q_len + t;
       tl[1]++;
       toks.push_back(q.q_off + t);
       toks.push_back(q.kv_len - q.q_len + t);
@@ -264,7 +266,11 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     for (int k = sc.tile_tr_begin[t]; k < sc.tile_tr_begin[t + 1]; ++k) {
       const TileReq& tr = sc.trs[k];
       const Req& q = rq[tr.r];
-      if (q.kv_len > q.shared_len) sc.tjobs.push_back({q.row, q.shared_len, q.kv_len, tr.lo, tr.hi, 1});
+      // causal: no token of this tile sees keys past its last position, so
+      // the job ends there (a causal prefill tile reads only the blocks up
+      // to its diagonal)
+      if (q.kv_len > q.shared_len)
+        sc.tjobs.push_back({q.row, q.shared_len, std::min(q.kv_len, tr.pmax + 1), tr.lo, tr.hi, 1});
     }
   }
   sc.tile_job_begin.push_back((int)sc.tjobs.size());
@@ -324,10 +330,12 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
       heap.push_back({piece(t), t});
       std::push_heap(heap.begin(), heap.end());
     }
-  } else if (ntiles > per_kvh && ntiles % per_kvh != 0 && per_kvh / (ntiles % per_kvh) >= 4) {
-    // more tiles than one round of workgroups and a short last round of e
-    // tiles per KV head: that round would leave most CUs idle for a whole
-    // tile's time.  The last e tiles (dispatched last) are cut into
+  } else if (ntiles > per_kvh && ntiles % per_kvh != 0 && per_kvh / (ntiles % per_kvh) >= 4 &&
+             *std::max_element(tcost.begin(), tcost.end()) <= 2 * *std::min_element(tcost.begin(), tcost.end())) {
+    // more tiles than one round of workgroups, of similar cost (within 2x),
+    // and a short last round of e tiles per KV head: that round would leave
+    // most CUs idle for a whole tile's time (tiles of varied cost, as in a
+    // causal prefill, even out by longest-first dispatch instead).  The last e tiles (dispatched last) are cut into
     // per_kvh / e pieces each, so the last round is full with pieces of a
     // quarter of a tile or less.  Measured on MI355X (extend, 256-row
     // tiles): 10 tiles per head on 8 slots, last 2 in quarters, 116 -> 98 us
@@ -413,8 +421,42 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     }
   }
   key_rows *= hkv;
-  // longest items first (all KV heads of an item next to each other)
-  std::stable_sort(its.begin(), its.end(), [](const ItemRec& a, const ItemRec& c) { return a.cost > c.cost; });
+  // Dispatch order (all KV heads of an item next to each other).  Items are
+  // grouped by the key stream their tile starts with -- the page-table row
+  // of its first job: a shared prefix, or the request's own causal range --
+  // streams ordered by their longest item (then first appearance), and
+  // within a stream the longest items first.  Workgroup i*Hkv + h runs on
+  // XCD (i*Hkv + h) mod 8, so the items one XCD runs at a time are
+  // consecutive records: grouped by stream they read the same keys at
+  // about the same time and share that XCD's L2.  Ordered by length alone,
+  // a causal prefill interleaves every sequence's longest tiles, and each
+  // of an XCD's workgroups streams a different sequence.
+  {
+    static thread_local std::vector<int64_t> key_of_tile, smax, sfirst;
+    key_of_tile.assign(ntiles, 0);
+    smax.clear();
+    sfirst.clear();
+    // stream index per tile: consecutive tiles with the same first-job row
+    // share one (a stream's tiles are consecutive: requests are ordered by
+    // their segments, a request's tiles follow each other)
+    int32_t prev_row = INT32_MIN;
+    for (int t = 0; t < ntiles; ++t) {
+      const int32_t row = sc.tile_job_begin[t] == sc.tile_job_begin[t + 1] ? INT32_MIN + 1 + t
+                                                                          : sc.tjobs[sc.tile_job_begin[t]].row;
+      if (t == 0 || row != prev_row) {
+        smax.push_back(0);
+        sfirst.push_back(t);
+      }
+      prev_row = row;
+      key_of_tile[t] = (int64_t)smax.size() - 1;
+    }
+    for (auto& it : its) smax[key_of_tile[it.tile]] = std::max<int64_t>(smax[key_of_tile[it.tile]], it.cost);
+    std::stable_sort(its.begin(), its.end(), [&](const ItemRec& a, const ItemRec& c) {
+      const int64_t sa = key_of_tile[a.tile], sb = key_of_tile[c.tile];
+      if (sa != sb) return smax[sa] != smax[sb] ? smax[sa] > smax[sb] : sfirst[sa] < sfirst[sb];
+      return a.cost > c.cost;
+    });
+  }
   // one record per chunk; the launch runs record i for KV heads 0..Hkv-1 as
   // workgroups i*Hkv .. i*Hkv+Hkv-1
   for (auto& it : its) {
