@@ -422,19 +422,20 @@ __device__ __forceinline__ void wave_block(const KVTile<D>& t, const bf16x8 (&qr
   wave_update<D>(t, s, acc, m_run, l_run, rel, c2, li, hi);
 }
 
-// Final result of one lane's row: the normalised output (direct tiles) or
-// the partial state (split tiles, contribution item[3]).
+// Final result of one lane's row: the normalised output (direct tiles; its
+// caller Q/O row q_index) or the partial state (split tiles: the item's
+// contribution covers tile tokens [act_lo, act_hi) at workspace token
+// ws_base).
 template <int D>
-__device__ __forceinline__ void write_result(const AttnArgs& a, const int32_t* tile, const int32_t* item, int kvh,
-                                             const f32x16 (&acc)[D / 32], float m_run, float l_run, bool row_ok,
-                                             int tloc, int row, int hi) {
+__device__ __forceinline__ void write_result(const AttnArgs& a, bool split, int act_lo, int act_hi, int ws_base,
+                                             int32_t q_index, int kvh, const f32x16 (&acc)[D / 32], float m_run,
+                                             float l_run, bool row_ok, int tloc, int row, int hi) {
   constexpr int DB = D / 32;
-  const int group = a.group, tok_begin = tile[0];
+  const int group = a.group;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (tile[4] < 0) {
+  if (!split) {
     if (row_ok) {
-      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
       __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -448,9 +449,8 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const int32_t* t
     }
     return;
   }
-  const int32_t* cr = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
-  if (row_ok && tloc >= cr[0] && tloc < cr[1]) {
-    const int64_t w = ((int64_t)kvh * a.ws_tokens + cr[2] + tloc - cr[0]) * group + row % group;
+  if (row_ok && tloc >= act_lo && tloc < act_hi) {
+    const int64_t w = ((int64_t)kvh * a.ws_tokens + ws_base + tloc - act_lo) * group + row % group;
     float* dst = a.ws_o + w * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -464,7 +464,6 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const int32_t* t
       a.ws_ml[w * 2 + 1] = l_tot;
     }
   }
-
 }
 
 template <int D, bool OFF32>
@@ -621,7 +620,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  write_result<D>(a, tile, item, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
+  const int32_t q_index = row_ok ? a.toks[(int64_t)(tok_begin + tloc) * kTokWords] : 0;
+  write_result<D>(a, item[7] >= 0, item[8], item[9], item[10], q_index, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -988,11 +988,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
 
   // one item record per key chunk, run for every KV head: workgroup b takes
   // record b / Hkv and KV head b % Hkv
+  // everything the workgroup needs to start comes from its item record:
+  // token range, contribution, block count, the first job and, when the
+  // tile's caller rows are consecutive, its first Q row (the Q loads then
+  // go out after this one read)
   const int32_t* item = a.items + (int64_t)(blockIdx.x / (unsigned)a.hkv) * kItemWords;
-  const int32_t* tile = a.tiles + (int64_t)item[0] * kTileWords;
   const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
-  const int jb = item[1], je = item[2];
-  const int tok_begin = tile[0], n_tok = tile[1];
+  const int jb = item[1], je = item[2], nblk = item[4];
+  const int tok_begin = item[5], n_tok = item[6];
+  const int act_lo = item[8], act_hi = item[9];
   const int group = a.group;
   const int n_rows = n_tok * group;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1000,22 +1004,18 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   const int li = lane & 31, hi = lane >> 5;
   const int row = wave * 32 + li;
   const int tloc = row / group;
-  int act_lo = 0, act_hi = n_tok;
-  if (tile[4] >= 0) {
-    const int32_t* cr0 = a.contribs + (int64_t)(tile[3] + item[3]) * kContribWords;
-    act_lo = cr0[0];
-    act_hi = cr0[1];
-  }
   const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
   const bool wave_live = __ballot(row_ok) != 0;
 
   bf16x8 qreg[KSTEPS];
   int qpos = 0;
+  int32_t q_index = 0;
   if (row_ok) {
     const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
+    q_index = item[17] >= 0 ? item[17] + tloc : tk[0];
     qpos = tk[1];
     const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
-                        ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
+                        ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
   } else {
@@ -1033,12 +1033,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   const uint32_t off = (uint32_t)(kvh * D + 8 * cc) * 2;
   const int vcol = vt_col(qd);
 
-  int nblk = 0;
-  for (int j = jb; j < je; ++j) {
-    const int32_t* job = a.jobs + (int64_t)j * kJobWords;
-    nblk += (job[2] - job[1] + 63) >> 6;
-  }
-
   auto issue = [&](Rows4& r, const int* slots, bool valid = true) {
     const int4 sl = *reinterpret_cast<const int4*>(slots + 4 * qd);
     r = pool.rows_if(sl, off, valid);
@@ -1052,7 +1046,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
 
   if (nblk > 0) {
     BlockIter it_slot, it_comp, it_next;
-    iter_job(a, it_slot, jb);
+    it_slot.j = jb;
+    it_slot.prow = a.page_table + (int64_t)item[11] * a.ld;
+    it_slot.kb = item[12];
+    it_slot.k1 = item[13];
     it_comp = it_slot;
     Rows4 rA, rB;
     // ---- prologue: blocks 0 and 1 in LDS, block 2 loading, slots of block 3 in the ring ----
@@ -1084,7 +1081,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
     it_next = it_comp;
     iter_next(a, it_next, je);
     f32x16 s[2];
-    job_view(a, it_comp, vc, row_ok, tloc, qpos, wave_live);
+    // the first job's view from the item record
+    vc.job = jb;
+    vc.lim = (row_ok && tloc >= item[14] && tloc < item[15]) ? (item[16] ? min(item[13], qpos + 1) : item[13]) : 0;
+    vc.live = wave_live && __ballot(vc.lim > item[12]) != 0;
     if (ahead && vc.live) wave_scores<D>(buf[0], qreg, s, li, hi);
 
     int bc = 0;  // LDS buffer of block b
@@ -1124,7 +1124,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
       step(b + 1, rA, rB);
     }
   }
-  write_result<D>(a, tile, item, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
+  write_result<D>(a, item[7] >= 0, act_lo, act_hi, item[10], q_index, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
 }
 
 // ---------------------------------------------------------------------------

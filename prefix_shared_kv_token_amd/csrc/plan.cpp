@@ -471,8 +471,13 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
       base = cr[2];
     }
     const int32_t* j0 = &jobs[(int64_t)it.jb * kJobWords];
+    // the tile's first caller Q row when its tokens' rows are consecutive
+    // (the kernels then address Q without the token records), else -1
+    int32_t q0 = toks[(int64_t)tl[0] * kTokWords];
+    for (int32_t k = 1; k < tl[1] && q0 >= 0; ++k)
+      if (toks[(int64_t)(tl[0] + k) * kTokWords] != q0 + k) q0 = -1;
     items.insert(items.end(), {it.tile, it.jb, it.je, it.c, nb, tl[0], tl[1], tl[4], lo, hi, base, j0[0], j0[1],
-                               j0[2], j0[3], j0[4], j0[5], 0, 0, 0});
+                               j0[2], j0[3], j0[4], j0[5], q0, 0, 0});
   }
 
   // ---- workspace ----

@@ -26,7 +26,9 @@ constexpr int kDecodeTileRows = 64;  // query rows per tile of the bf16 decode k
 // the item; 5-7: the tile's tok_begin, n_tok, split index (-1: none); 8-10:
 // the contribution's tok_lo, tok_hi, ws_token_base (0, n_tok, 0 unsplit);
 // 11-16: the first job (page_row, key_begin, key_end, tok_lo, tok_hi,
-// causal) -- everything a workgroup needs to start loading in one read.
+// causal); 17: the caller Q row of the tile's first token when the tile's
+// rows are consecutive, else -1 -- everything a workgroup needs to start
+// loading in one read.
 constexpr int kItemWords = 20;
 constexpr int kTileWords = 8;     // tok_begin, n_tok, n_contrib, contrib_begin, split index (-1: none), cptr base
 constexpr int kJobWords = 8;      // page_row, key_begin, key_end, tok_lo, tok_hi, causal
