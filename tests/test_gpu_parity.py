@@ -215,3 +215,16 @@ def test_full_size_sampled(cfg):
         mid = wl.phases[1].requests
         extra = [mid[0].rid, mid[len(mid) // 2].rid, mid[-1].rid]
     run_and_check(cfg, sample_leaves=FULL_SAMPLES[cfg.name], leaf_extra=extra)
+
+
+def test_decode_long_items():
+    """Decode items of 56+ key blocks (a 3,500-token prefix shared by 4
+    requests, one decode item per KV head): every output against the
+    oracle, on the 32-bit and the 64-bit (scattered pool over 2 GiB,
+    NaN-poisoned) paths."""
+    cfg = config_by_name("batchllm").replace(levels=((1, 3500), (4, 9)), decode_steps=3)
+    run, _, _ = run_and_check(cfg, decode_items=8)
+    assert run.rt._info.num_items == 8   # the last decode step's plan: one item per KV head
+    row_bytes = 8 * 128 * 2
+    extra = (1 << 31) // row_bytes + 4096
+    run_and_check(cfg, decode_items=8, hole_seed=3, extra_slots=extra, poison=True)
