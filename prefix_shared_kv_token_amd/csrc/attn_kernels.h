@@ -189,6 +189,7 @@ struct Rows4 {
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Reads 16-byte chunks of pool rows.  OFF32: the pool is under 4 GiB and is
 // addressed through a raw buffer resource with 32-bit byte offsets
@@ -435,18 +436,29 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, bool split, int 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!split) {
-    if (row_ok) {
-      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
+    // Lane (row, hi) holds d = 32 db + 8 g4 + 4 hi + (0..3).  Pairs of
+    // 4-value pieces are exchanged with lane ^ 32 (v_permlane32_swap), so
+    // each lane stores whole 16-byte runs: hi = 0 the 8 values of g4 = 2p,
+    // hi = 1 those of g4 = 2p + 1 (half the store instructions).
+    __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 v;
+      for (int p = 0; p < 2; ++p) {
+        bf16x4 v0, v1;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hi) = v;
+        for (int e = 0; e < 4; ++e) {
+          v0[e] = (__bf16)(acc[db][8 * p + e] * inv);
+          v1[e] = (__bf16)(acc[db][8 * p + 4 + e] * inv);
         }
-    }
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+        const auto x = __builtin_amdgcn_permlane32_swap(w0.x, w1.x, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(w0.y, w1.y, false, false);
+        // hi = 0: its own piece of g4 = 2p, then its partner's; hi = 1: its
+        // partner's piece of g4 = 2p + 1, then its own
+        const u32x4 out = u32x4{x[0], y[0], x[1], y[1]};
+        if (row_ok) *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * p + 8 * hi) = out;
+      }
     return;
   }
   if (row_ok && tloc >= act_lo && tloc < act_hi) {
@@ -641,7 +653,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct DecTile {
