@@ -283,3 +283,41 @@ def test_multilevel_decode_tiles():
     own = sum(int(j[2] - j[1]) for j in v["jobs"] if j[5] == 1)
     assert shared == 1024 * 2 + 512 * 9
     assert own == 24 * (128 + 1)
+
+
+@pytest.mark.parametrize("group", [1, 4])
+def test_causal_jobs_end_at_the_tiles_last_query(group):
+    """A causal prefill (every prompt token new, no cached prefix): a tile's own
+    job reads keys only up to its last query position (the coverage check
+    fixes that it reads all of them), so a tile iterates no key block that
+    is masked for every one of its rows."""
+    cfg = config_by_name("batchllm").replace(levels=((3, 700),), decode_steps=1, n_q_heads=8,
+                                             n_kv_heads=8 // group)
+    wl = Workload(cfg)
+    tree = rdx.Tree(cfg.total_tokens())
+    reqs = []
+    for r in wl.phases[0].requests:
+        p = wl.prompt_tokens(r)
+        m, slots, node = tree.match_prefix(p)
+        assert m == 0
+        tree.lock(node)
+        reqs.append((p, m, node, tree.alloc(len(p)).copy()))
+    hkv = 8 // group
+    desc = rdx.attn_desc(rdx.BF16, 8, hkv, 128, cfg.total_tokens())
+    plan = rdx.Plan(desc, rdx.PLAN_EXTEND)
+    kv_len = [len(p) for p, *_ in reqs]
+    new = np.concatenate([row for *_, row in reqs])
+    rows = list(range(len(reqs)))
+    plan.build(tree, [n for _, _, n, _ in reqs], rows, kv_len, kv_len, [0] * len(reqs), new, cfg.max_seq_len)
+    v = _check_coverage(plan, kv_len, kv_len, rows, hkv)
+    tiles, jobs, toks = v["tiles"], v["jobs"], v["tokens"]
+    n_items_jobs = 0
+    for it in v["items"]:
+        tile = tiles[it[0]]
+        pmax = max(int(toks[tile[0] + t, 1]) for t in range(tile[1]))
+        for jb in range(it[1], it[2]):
+            j = jobs[jb]
+            n_items_jobs += 1
+            assert j[5] == 1                   # all keys are the request's own: causal
+            assert j[2] <= pmax + 1            # ends at the tile's last query
+    assert n_items_jobs > 0
