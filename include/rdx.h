@@ -254,13 +254,24 @@ typedef struct rdx_attn_desc {
   int32_t num_kv_heads; /* Hkv, divides Hq; query head h reads KV head h*Hkv/Hq */
   int32_t head_dim;     /* 64 or 128 */
   float sm_scale;       /* 0 -> 1/sqrt(head_dim) */
-  int32_t reserved;
+  int32_t kv_row_pitch; /* elements from one slot's row to the next in each KV
+                           pool: 0 = Hkv*head_dim (dense), else >= Hkv*head_dim
+                           with pitch*element size a multiple of 16 bytes */
   int64_t num_slots;    /* rows of each KV pool */
 } rdx_attn_desc;
-/* Layouts (row-major, contiguous):
- *   K pool, V pool   [num_slots][Hkv][head_dim]
+/* Layouts (row-major):
+ *   K pool, V pool   [num_slots][pitch] elements, slot s's [Hkv][head_dim]
+ *                    at the start of row s (pitch = kv_row_pitch or dense)
  *   Q, O, new K/V    [tokens][H][head_dim]   (H = Hq for Q/O, Hkv for K/V)
  *   page table       int32 [rows][ld]: row r, position p -> slot  */
+
+/* The row pitch the kernels stream fastest (elements; a caller allocates its
+ * pools with it and stores it in kv_row_pitch).  Each workgroup reads one KV
+ * head's slice of every row it visits; with a dense row of a multiple of
+ * 1 KiB, some heads' slices fall on the same few memory channels for every
+ * row and stream ~25 % slower than the others, so the rows are padded by
+ * 256 bytes.  desc->kv_row_pitch is ignored.  Errors: EINVAL. */
+int rdx_kv_row_pitch_recommended(const rdx_attn_desc* desc, int32_t* out);
 
 /* Scatter new K/V rows into the pools: pool[slots[i]] = new[i], i < n.
  * slots: device int32[n], distinct.  Errors: EINVAL, EUNSUPPORTED, EDEVICE. */
@@ -408,7 +419,7 @@ typedef struct rdx_step_io {
   int64_t workspace_bytes;
   int32_t* page_table;       /* device int32 [page_table_rows][ld] */
   int64_t page_table_rows;
-  void* k_pool;              /* device [num_slots][Hkv][head_dim] each */
+  void* k_pool;              /* device [num_slots][pitch] each (desc->kv_row_pitch) */
   void* v_pool;
   const void* q;             /* device [num_reqs][Hq][head_dim] */
   const void* k_new;         /* device [num_reqs][Hkv][head_dim] each */

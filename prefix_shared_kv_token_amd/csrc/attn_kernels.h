@@ -52,6 +52,7 @@ struct AttnArgs {
   float* ws_ml;
   int64_t ws_tokens;
   int64_t pool_bytes;  // bytes of each KV pool
+  int32_t row_bytes;   // bytes from one slot's row of a pool to the next
   int hq, hkv, group;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = a.scale_log2;
 
-  const uint32_t row_bytes = (uint32_t)(a.hkv * D * 2);
+  const uint32_t row_bytes = (uint32_t)a.row_bytes;
   PoolReader<OFF32> kpool, vpool;
   kpool.init(a.kp, a.pool_bytes, row_bytes);
   vpool.init(a.vp, a.pool_bytes, row_bytes);
@@ -691,7 +692,7 @@ struct DecPool {
   const char *kb, *vb;
   uint32_t row_bytes;
   __device__ void init(const AttnArgs& a) {
-    row_bytes = (uint32_t)(a.hkv * D * 2);
+    row_bytes = (uint32_t)a.row_bytes;
     kb = reinterpret_cast<const char*>(a.kp);
     vb = reinterpret_cast<const char*>(a.vp);
     if constexpr (OFF32) {
@@ -1040,7 +1041,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   const float c2 = a.scale_log2;
 
   PoolReader<OFF32> pool;
-  pool.init(doK ? a.kp : a.vp, a.pool_bytes, (uint32_t)(a.hkv * D * 2));
+  pool.init(doK ? a.kp : a.vp, a.pool_bytes, (uint32_t)a.row_bytes);
   const uint32_t off = (uint32_t)(kvh * D + 8 * cc) * 2;
   const int vcol = vt_col(qd);
 
@@ -1169,7 +1170,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
     const int32_t* prow = a.page_table + (int64_t)job[0] * a.ld;
     const int end = job[5] ? min(job[2], qpos + 1) : job[2];
     for (int p = job[1]; p < end; ++p) {
-      const int64_t off = ((int64_t)prow[p] * a.hkv + kvh) * D;
+      const int64_t off = (int64_t)prow[p] * (a.row_bytes / 4) + (int64_t)kvh * D;
       float s = 0.f;
       for (int d = 0; d < D; ++d) s = fmaf(q[d], kpool[off + d], s);
       const float t = s * a.scale_log2;
@@ -1199,13 +1200,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // KV scatter and page-table writes
 // ---------------------------------------------------------------------------
+// New rows arrive dense (row_vecs 16-byte vectors each); a pool row is
+// pitch_vecs vectors apart.
 __global__ void kv_store_kernel(uint4* __restrict__ kp, uint4* __restrict__ vp, const uint4* __restrict__ kn,
                                 const uint4* __restrict__ vn, const int32_t* __restrict__ slots, int64_t n,
-                                int64_t row_vecs) {
+                                int64_t row_vecs, int64_t pitch_vecs) {
   const int64_t total = n * row_vecs;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t tok = i / row_vecs, e = i % row_vecs;
-    const int64_t dst = (int64_t)slots[tok] * row_vecs + e;
+    const int64_t dst = (int64_t)slots[tok] * pitch_vecs + e;
     kp[dst] = kn[i];
     vp[dst] = vn[i];
   }
@@ -1240,7 +1243,8 @@ __global__ void step_store_kernel(const int4* __restrict__ stage, int4* __restri
                                   const int32_t* __restrict__ runs, const int32_t* __restrict__ run_slots,
                                   int32_t n_runs, uint4* __restrict__ kp, uint4* __restrict__ vp,
                                   const uint4* __restrict__ kn, const uint4* __restrict__ vn,
-                                  const int32_t* __restrict__ slots, int64_t n, int64_t row_vecs) {
+                                  const int32_t* __restrict__ slots, int64_t n, int64_t row_vecs,
+                                  int64_t pitch_vecs) {
   const int32_t bx = (int32_t)blockIdx.x;
   if (bx < n_copy) {
     for (int64_t i = (int64_t)bx * blockDim.x + threadIdx.x; i < n_vec4; i += (int64_t)n_copy * blockDim.x)
@@ -1269,7 +1273,7 @@ __global__ void step_store_kernel(const int4* __restrict__ stage, int4* __restri
   const int64_t nb = (int64_t)gridDim.x - n_copy - n_pt;
   for (int64_t i = ((int64_t)bx - n_copy - n_pt) * blockDim.x + threadIdx.x; i < total; i += nb * blockDim.x) {
     const int64_t tok = i / row_vecs, e = i % row_vecs;
-    const int64_t dst = (int64_t)slots[tok] * row_vecs + e;
+    const int64_t dst = (int64_t)slots[tok] * pitch_vecs + e;
     kp[dst] = kn[i];
     vp[dst] = vn[i];
   }

@@ -252,6 +252,20 @@ int check_desc(const rdx_attn_desc* d) {
   if (d->head_dim != 64 && d->head_dim != 128) return fail(RDX_EUNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
   if (d->num_slots <= 0 || d->num_slots >= ((int64_t)1 << 31)) return fail(RDX_EINVAL, "num_slots out of range");
   if (!(d->sm_scale >= 0.f) || std::isinf(d->sm_scale)) return fail(RDX_EINVAL, "sm_scale must be finite and >= 0");
+  if (d->kv_row_pitch < 0 || (d->kv_row_pitch > 0 && (d->kv_row_pitch < (int64_t)d->num_kv_heads * d->head_dim ||
+                                                       (d->kv_row_pitch * kv_elem_bytes(d)) % 16)))
+    return fail(RDX_EINVAL, "kv_row_pitch %d: 0, or >= Hkv*head_dim with 16-byte rows", d->kv_row_pitch);
   return ok();
 }
 }  // namespace rdx
+
+int rdx_kv_row_pitch_recommended(const rdx_attn_desc* desc, int32_t* out) {
+  if (!desc || !out) return fail(RDX_EINVAL, "rdx_kv_row_pitch_recommended: null argument");
+  rdx_attn_desc d = *desc;
+  d.kv_row_pitch = 0;
+  int rc = rdx::check_desc(&d);
+  if (rc) return rc;
+  const int64_t es = rdx::kv_elem_bytes(&d), dense = (int64_t)d.num_kv_heads * d.head_dim;
+  *out = (int32_t)((dense * es) % 1024 == 0 ? dense + 256 / es : dense);
+  return rdx::ok();
+}

@@ -148,7 +148,8 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
   a.ws_o = reinterpret_cast<float*>(wsb);
   a.ws_ml = wsb ? reinterpret_cast<float*>(wsb + p->ws_ml_offset) : nullptr;
   a.ws_tokens = p->ws_tokens;
-  a.pool_bytes = desc->num_slots * desc->num_kv_heads * desc->head_dim * (desc->dtype == RDX_BF16 ? 2 : 4);
+  a.row_bytes = (int32_t)(kv_row_elems(desc) * kv_elem_bytes(desc));
+  a.pool_bytes = desc->num_slots * a.row_bytes;
   a.hq = desc->num_q_heads;
   a.hkv = desc->num_kv_heads;
   a.group = a.hq / a.hkv;
@@ -298,7 +299,8 @@ int rdx_kv_store(const rdx_attn_desc* desc, void* k_pool, void* v_pool, const vo
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(kv_store_kernel, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      reinterpret_cast<uint4*>(k_pool), reinterpret_cast<uint4*>(v_pool),
-                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new), slots, n, row_vecs);
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new), slots, n, row_vecs,
+                     kv_row_elems(desc) * esize / 16);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "rdx_kv_store launch");
   return ok();
@@ -368,6 +370,7 @@ static int store_and_attend(Plan* p, rdx_plan* hplan, const rdx_attn_desc* desc,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t n_runs = (int64_t)p->runs.size() / kRunWords;
   const int64_t row_vecs = row_bytes / 16, total = num_new * row_vecs;
+  const int64_t pitch_vecs = kv_row_elems(desc) * esize / 16;
   // The fused kernel reads the staged list through PCIe: right for a decode
   // step (a few KB, one page-table entry per run).  A batch that admits
   // requests writes whole rows and carries a large list: copy it by DMA,
@@ -381,7 +384,7 @@ static int store_and_attend(Plan* p, rdx_plan* hplan, const rdx_attn_desc* desc,
       hipLaunchKernelGGL(kv_store_kernel, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint4*>(io->k_pool),
                          reinterpret_cast<uint4*>(io->v_pool), reinterpret_cast<const uint4*>(io->k_new),
                          reinterpret_cast<const uint4*>(io->v_new),
-                         reinterpret_cast<const int32_t*>(io->dev_plan) + p->off_new, num_new, row_vecs);
+                         reinterpret_cast<const int32_t*>(io->dev_plan) + p->off_new, num_new, row_vecs, pitch_vecs);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(e, "KV store launch");
     }
@@ -402,7 +405,7 @@ static int store_and_attend(Plan* p, rdx_plan* hplan, const rdx_attn_desc* desc,
                      (int32_t)n_copy, io->page_table, ld, hs + p->off_runs, hs + p->off_run_slots, (int32_t)n_runs,
                      reinterpret_cast<uint4*>(io->k_pool), reinterpret_cast<uint4*>(io->v_pool),
                      reinterpret_cast<const uint4*>(io->k_new), reinterpret_cast<const uint4*>(io->v_new),
-                     hs + p->off_new, num_new, row_vecs);
+                     hs + p->off_new, num_new, row_vecs, pitch_vecs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "step store launch");
   rc = stage_done(p, st);

@@ -42,7 +42,7 @@ class NodeInfo(ctypes.Structure):
 
 class AttnDesc(ctypes.Structure):
     _fields_ = [("dtype", i32), ("num_q_heads", i32), ("num_kv_heads", i32), ("head_dim", i32),
-                ("sm_scale", ctypes.c_float), ("reserved", i32), ("num_slots", i64)]
+                ("sm_scale", ctypes.c_float), ("kv_row_pitch", i32), ("num_slots", i64)]
 
 
 class Batch(ctypes.Structure):
@@ -103,6 +103,7 @@ _SIGS = {
     "rdx_tree_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats)]),
     "rdx_node_get": (ctypes.c_int, [vp, i64, ctypes.POINTER(NodeInfo), i32p]),
     "rdx_kv_store": (ctypes.c_int, [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, vp]),
+    "rdx_kv_row_pitch_recommended": (ctypes.c_int, [ctypes.POINTER(AttnDesc), i32p]),
     "rdx_plan_create": (ctypes.c_int, [ctypes.POINTER(AttnDesc), i32, i32, ctypes.POINTER(vp)]),
     "rdx_plan_destroy": (None, [vp]),
     "rdx_plan_build": (ctypes.c_int, [vp, vp, ctypes.POINTER(Batch), i64]),
@@ -388,8 +389,14 @@ class Job:
 
 # --------------------------------------------------------------------- plan
 def attn_desc(dtype: int, num_q_heads: int, num_kv_heads: int, head_dim: int, num_slots: int,
-              sm_scale: float = 0.0) -> AttnDesc:
-    return AttnDesc(dtype, num_q_heads, num_kv_heads, head_dim, sm_scale, 0, num_slots)
+              sm_scale: float = 0.0, kv_row_pitch: int = 0) -> AttnDesc:
+    return AttnDesc(dtype, num_q_heads, num_kv_heads, head_dim, sm_scale, kv_row_pitch, num_slots)
+
+
+def kv_row_pitch_recommended(desc: AttnDesc) -> int:
+    out = i32(0)
+    _check(lib().rdx_kv_row_pitch_recommended(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
 
 
 class Plan:

@@ -119,10 +119,14 @@ class Runtime:
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.desc = rdx.attn_desc(rdx.BF16 if dtype == "bf16" else rdx.F32, num_q_heads, num_kv_heads,
                                   head_dim, num_slots)
+        # pools with the row pitch the kernels stream fastest (rows padded past
+        # the Hkv x head_dim a slot holds)
+        self.kv_row_pitch = rdx.kv_row_pitch_recommended(self.desc)
+        self.desc.kv_row_pitch = self.kv_row_pitch
         self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_dim
         self.num_slots, self.ld, self.max_rows = num_slots, ld, max_rows
         self.tree = rdx.Tree(num_slots)
-        self.k_pool = torch.zeros((num_slots, num_kv_heads, head_dim), dtype=self.tdtype, device=self.device)
+        self.k_pool = torch.zeros((num_slots, self.kv_row_pitch), dtype=self.tdtype, device=self.device)
         self.v_pool = torch.zeros_like(self.k_pool)
         self.page_table = torch.zeros((max_rows, ld), dtype=torch.int32, device=self.device)
         self.host_pt = np.zeros((max_rows, ld), np.int32)

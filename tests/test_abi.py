@@ -71,6 +71,26 @@ def test_descriptor_errors():
     assert e.value.code == rdx.EINVAL
 
 
+def test_kv_row_pitch():
+    """Rows padded by 256 bytes when the dense row is a multiple of 1 KiB;
+    a pitch below the dense row or not a whole number of 16 bytes is
+    rejected, and so is a negative one."""
+    assert rdx.kv_row_pitch_recommended(rdx.attn_desc(rdx.BF16, 32, 8, 128, 100)) == 8 * 128 + 128
+    assert rdx.kv_row_pitch_recommended(rdx.attn_desc(rdx.BF16, 32, 32, 128, 100)) == 32 * 128 + 128
+    assert rdx.kv_row_pitch_recommended(rdx.attn_desc(rdx.F32, 4, 4, 64, 100)) == 4 * 64 + 64
+    assert rdx.kv_row_pitch_recommended(rdx.attn_desc(rdx.BF16, 6, 3, 64, 100)) == 3 * 64  # 384 B: dense
+    # the descriptor's own pitch is ignored by the recommendation
+    assert rdx.kv_row_pitch_recommended(rdx.attn_desc(rdx.BF16, 32, 8, 128, 100, kv_row_pitch=-5)) == 8 * 128 + 128
+    rdx.Plan(rdx.attn_desc(rdx.BF16, 32, 8, 128, 100, kv_row_pitch=8 * 128 + 8), rdx.PLAN_EXTEND)
+    for bad in (-1, 8 * 128 - 8, 8 * 128 + 4):
+        with pytest.raises(rdx.RdxError) as e:
+            rdx.Plan(rdx.attn_desc(rdx.BF16, 32, 8, 128, 100, kv_row_pitch=bad), rdx.PLAN_EXTEND)
+        assert e.value.code == rdx.EINVAL
+    with pytest.raises(rdx.RdxError) as e:
+        rdx.kv_row_pitch_recommended(rdx.attn_desc(rdx.BF16, 32, 8, 96, 100))
+    assert e.value.code == rdx.EUNSUPPORTED
+
+
 def test_plan_build_rejects_inconsistent_batches():
     t = rdx.Tree(64)
     m, slots, node = t.match_prefix(np.arange(10))

@@ -150,8 +150,10 @@ def test_deterministic_and_kv_store_roundtrip():
     leaf = wl.leaf_requests[1]
     row = a["rows"][-1][1]
     k_log, v_log = wl.request_full_kv(leaf)
-    kp = run.rt.k_pool[torch.as_tensor(row, device=run.rt.device).long()].float().cpu().numpy()
-    vp = run.rt.v_pool[torch.as_tensor(row, device=run.rt.device).long()].float().cpu().numpy()
+    idx = torch.as_tensor(row, device=run.rt.device).long()
+    hd = cfg.n_kv_heads * cfg.head_dim  # a pool row holds the slot's [Hkv][D] first, then padding
+    kp = run.rt.k_pool[idx][:, :hd].reshape(len(row), cfg.n_kv_heads, cfg.head_dim).float().cpu().numpy()
+    vp = run.rt.v_pool[idx][:, :hd].reshape(len(row), cfg.n_kv_heads, cfg.head_dim).float().cpu().numpy()
     np.testing.assert_array_equal(kp, k_log)
     np.testing.assert_array_equal(vp, v_log)
 
