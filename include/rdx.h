@@ -339,11 +339,12 @@ int rdx_plan_get_info(const rdx_plan* plan, rdx_plan_info* out);
 
 /* Copy the plan to dev_plan (device, >= device_bytes) on `stream` and write
  * the batch's page-table entries into page_table (device int32
- * [page_table_rows][ld]).  The plan stages uploads through a ring of 8
- * pinned host buffers, read by a copy kernel through their device mapping
- * (no DMA copy); the call blocks only while the upload made 8 calls earlier
- * has not left its buffer yet, and grows the ring (pinned allocations) when
- * a plan outgrows it.  Errors: EINVAL, EDEVICE. */
+ * [page_table_rows][ld]).  The plan stages uploads through a ring of N
+ * pinned host buffers (N = 32 for decode plans, 8 for extend plans), read by
+ * a copy kernel through their device mapping (no DMA copy); the call blocks
+ * only while the upload made N calls earlier has not left its buffer yet,
+ * and grows the ring (pinned allocations) when a plan outgrows it.
+ * Errors: EINVAL, EDEVICE. */
 int rdx_plan_upload(rdx_plan* plan, void* dev_plan, int64_t dev_plan_bytes,
                     int32_t* page_table, int64_t page_table_rows, void* stream);
 

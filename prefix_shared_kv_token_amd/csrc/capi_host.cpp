@@ -196,6 +196,7 @@ int rdx_plan_create(const rdx_attn_desc* desc, int32_t kind, int32_t target_item
   p->desc = *desc;
   p->kind = kind;
   p->target_items = target_items;
+  if (kind == RDX_PLAN_DECODE) p->n_stages = rdx::Plan::kMaxStages;
   if (kind == RDX_PLAN_EXTEND && desc->dtype == RDX_BF16 && desc->head_dim == 128) p->tile_rows = 2 * rdx::kTileRows;
   // bf16 decode: 64-row tiles for the decode kernel (a group's new tokens x
   // the GQA group fit one tile whenever the group has at most 64 heads)

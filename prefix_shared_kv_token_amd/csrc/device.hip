@@ -190,7 +190,7 @@ int launch_attention(const rdx_attn_desc* desc, const rdx_plan* hplan, int32_t k
 // Marks the current staging buffer in use until the work queued so far on
 // `st` (the copy or kernel that reads it) has completed.
 int stage_done(Plan* p, hipStream_t st) {
-  Plan::Stage& sg = p->stages[p->uploads % Plan::kStages];
+  Plan::Stage& sg = p->stages[p->uploads % p->n_stages];
   hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(sg.event), st);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   sg.pending = true;
@@ -213,7 +213,7 @@ int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_t
   if (n_runs > 0 && (!page_table || page_table_rows <= p->max_page_row))
     return fail(RDX_EINVAL, "rdx_plan_upload: page table with more than %lld rows needed", (long long)p->max_page_row);
   hipError_t e;
-  Plan::Stage& sg = p->stages[p->uploads % Plan::kStages];
+  Plan::Stage& sg = p->stages[p->uploads % p->n_stages];
   if (!sg.event) {
     hipEvent_t ev;
     e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
@@ -231,7 +231,8 @@ int upload_plan(Plan* p, void* dev_plan, int64_t dev_plan_bytes, int32_t* page_t
     // with the plan (freeing pinned memory waits for the device; a buffer
     // still read by a queued copy stays valid)
     const int64_t want = bytes + bytes / 2 + 4096;
-    for (Plan::Stage& o : p->stages) {
+    for (int i = 0; i < p->n_stages; ++i) {
+      Plan::Stage& o = p->stages[i];
       if (o.bytes >= want) continue;
       if (o.pinned) p->retired.push_back(o.pinned);
       o.pinned = nullptr;

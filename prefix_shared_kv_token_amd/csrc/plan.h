@@ -62,15 +62,19 @@ struct Plan {
   bool built = false;
   // upload staging, owned by the plan: a ring of pinned host buffers, each
   // with the event of the last copy out of it, so the host can prepare the
-  // next uploads while earlier ones are still queued
-  static constexpr int kStages = 8;
+  // next uploads while earlier ones are still queued.  Decode plans keep 32
+  // steps queued (a few hundred KB of lists): enough device work to cover
+  // the host's completion and admission work between batches; extend plans
+  // (lists of megabytes) keep 8.
+  static constexpr int kMaxStages = 32;
+  int n_stages = 8;
   struct Stage {
     void* pinned = nullptr;
     void* pinned_dev = nullptr;  // the same memory as the device addresses it
     int64_t bytes = 0;
     void* event = nullptr;
     bool pending = false;
-  } stages[kStages];
+  } stages[kMaxStages];
   int64_t uploads = 0;
   std::vector<void*> retired;  // outgrown staging buffers, freed with the plan
 
