@@ -1019,21 +1019,44 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
   const bool wave_live = __ballot(row_ok) != 0;
 
+  // page-table slots of blocks 0-3, read first: loads retire in
+  // order for the wait counter, so the slot-ring writes of the prologue wait
+  // for these reads only, never for the K/V blocks or Q behind them
+  BlockIter it_slot;
+  it_slot.j = jb;
+  it_slot.prow = a.page_table + (int64_t)item[11] * a.ld;
+  it_slot.kb = item[12];
+  it_slot.k1 = item[13];
+  // (every wave reads them, without a lane condition, so no lane mask or
+  // register merge forces an early wait; positions past the item's last
+  // block read its last key's slot, which is valid)
+  int sl[4] = {0, 0, 0, 0};
+  if (nblk > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sl[i] = block_slot(it_slot, lane);
+      if (nblk > i) iter_next(a, it_slot, je);
+    }
+  }
+  // the lane's token record (caller row, position), read right behind them
+  const int tl = max(0, min(tloc, n_tok - 1));
+  const int2 tok = *reinterpret_cast<const int2*>(a.toks + (int64_t)(tok_begin + tl) * kTokWords);
+
+  // Q and the query position: loaded after the first K/V requests (below),
+  // without a branch or a select on the loaded values, so no wait for a
+  // page-table slot or a K/V block includes them.  Rows outside the tile's
+  // active range read their clamped token's row: finite values whose keys
+  // are all masked, and whose results are never written.
   bf16x8 qreg[KSTEPS];
   int qpos = 0;
-  int32_t q_index = 0;
-  if (row_ok) {
-    const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
-    q_index = item[17] >= 0 ? item[17] + tloc : tk[0];
-    qpos = tk[1];
+  auto load_q = [&]() {
+    const int32_t qi = item[17] >= 0 ? item[17] + tl : tok.x;
+    qpos = tok.y;
     const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
-                        ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
+                        ((int64_t)qi * a.hq + (int64_t)kvh * group + row % group) * D + 8 * hi;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
-  } else {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qreg[s] = bf16x8{};
-  }
+  };
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -1057,36 +1080,28 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
   };
 
   if (nblk > 0) {
-    BlockIter it_slot, it_comp, it_next;
-    it_slot.j = jb;
-    it_slot.prow = a.page_table + (int64_t)item[11] * a.ld;
-    it_slot.kb = item[12];
-    it_slot.k1 = item[13];
-    it_comp = it_slot;
+    BlockIter it_comp, it_next;
+    it_comp.j = jb;
+    it_comp.prow = a.page_table + (int64_t)item[11] * a.ld;
+    it_comp.kb = item[12];
+    it_comp.k1 = item[13];
     Rows4 rA, rB;
     // ---- prologue: blocks 0 and 1 in LDS, block 2 loading, slots of block 3 in the ring ----
-    if (tid < 64) slot_ring[0][tid] = block_slot(it_slot, tid);
-    iter_next(a, it_slot, je);
-    if (nblk > 1) {
-      if (tid < 64) slot_ring[1][tid] = block_slot(it_slot, tid);
-      iter_next(a, it_slot, je);
+    if (tid < 64) {
+      slot_ring[0][tid] = sl[0];
+      slot_ring[1][tid] = sl[1];
     }
     __syncthreads();
     issue(rA, slot_ring[0]);
     if (nblk > 1) issue(rB, slot_ring[1]);
+    load_q();
     __syncthreads();
-    if (nblk > 2) {
-      if (tid < 64) slot_ring[0][tid] = block_slot(it_slot, tid);
-      iter_next(a, it_slot, je);
-    }
+    if (nblk > 2 && tid < 64) slot_ring[0][tid] = sl[2];
     stage(buf[0], rA);
     if (nblk > 1) stage(buf[1], rB);
     __syncthreads();
     if (nblk > 2) issue(rA, slot_ring[0]);
-    if (nblk > 3) {  // ring[1] was last read before the second barrier
-      if (tid < 64) slot_ring[1][tid] = block_slot(it_slot, tid);
-      iter_next(a, it_slot, je);
-    }
+    if (nblk > 3 && tid < 64) slot_ring[1][tid] = sl[3];  // ring[1] was last read before the second barrier
     __syncthreads();
 
     JobView vc, vn;  // jobs of the block being finished and of the block after it
@@ -1136,6 +1151,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void attn_bf16_wide_kernel(AttnArg
       step(b + 1, rA, rB);
     }
   }
+  const int32_t q_index = row_ok ? (item[17] >= 0 ? item[17] + tloc : tok.x) : 0;
   write_result<D>(a, item[7] >= 0, act_lo, act_hi, item[10], q_index, kvh, acc, m_run, l_run, row_ok, tloc, row, hi);
 }
 
