@@ -15,6 +15,7 @@ before it.
     python3 bench_trace_summary.py trace <run_kernel_trace.csv> --phases N --runs R
     python3 bench_trace_summary.py pmc <FETCH run_counter_collection.csv> <WRITE ...csv> --phases N \\
         --fetch-factor F --write-factor W
+    python3 bench_trace_summary.py counters <pass1 csv> <pass2 csv> ... --phases N [--label "extend phase 1"]
 """
 from __future__ import annotations
 
@@ -111,6 +112,57 @@ def pmc(fetch_path, write_path, n_phases, ff, wf):
         print(f"traffic_bytes_per_launch[extend member]: {sum(per) / len(per):.0f}")
 
 
+def counters(paths, n_phases, label_prefix):
+    """Counter passes (rocprofv3 --pmc, one CSV per pass) over the same run:
+    the mean of each counter over the dispatches whose class starts with
+    label_prefix, then the derived shares.  GRBM_GUI_ACTIVE is summed over
+    the 8 XCDs (active cycles per XCD = GRBM / 8); SQ_*_CYCLES counters are
+    summed over the SIMDs (1,024) or CUs (256) as noted."""
+    vals = collections.defaultdict(list)
+    for path in paths:
+        rows = _rows_all(path)
+        disp = collections.OrderedDict()
+        for r in rows:
+            disp.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], {}))[1][r["Counter_Name"]] = float(r["Counter_Value"])
+        ids = sorted(disp)
+        labels = classify([disp[i][0] for i in ids], n_phases)
+        for i, lab in zip(ids, labels):
+            if lab.startswith(label_prefix):
+                for k, v in disp[i][1].items():
+                    vals[k].append(v)
+    m = {k: sum(v) / len(v) for k, v in vals.items()}
+    print("| counter | mean per dispatch |")
+    print("|---|---:|")
+    for k in sorted(m):
+        print(f"| {k} | {m[k]:,.0f} |")
+    grbm = [v for k, v in m.items() if k.startswith("GRBM_GUI_ACTIVE")]
+    if grbm:
+        act = grbm[0] / 8  # cycles per XCD
+        print()
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            print(f"MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1,024 SIMDs)): {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (act * 1024) * 100:.1f}%")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            print(f"MFMA and VALU co-executing (SQ_VALU_MFMA_COEXEC_CYCLES / (active cycles x 1,024)): {m['SQ_VALU_MFMA_COEXEC_CYCLES'] / (act * 1024) * 100:.1f}%")
+        if "SQ_ACTIVE_INST_VALU" in m:
+            print(f"VALU busy (SQ_ACTIVE_INST_VALU x 4 / (active cycles x 1,024), rocprof's VALUBusy): "
+                  f"{m['SQ_ACTIVE_INST_VALU'] * 4 / (act * 1024) * 100:.1f}%")
+        if "SQ_LDS_IDX_ACTIVE" in m:
+            print(f"LDS active (SQ_LDS_IDX_ACTIVE / (active cycles x 256 CUs)): {m['SQ_LDS_IDX_ACTIVE'] / (act * 256) * 100:.1f}%")
+        if "SQ_LDS_BANK_CONFLICT" in m and "SQ_LDS_IDX_ACTIVE" in m:
+            print(f"LDS bank-conflict share (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE): {m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE'] * 100:.1f}%")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+            print(f"executed bf16 MFMA flops (MOPS x 512): {m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e12:.3f} TFLOP")
+    if "SQ_INSTS_MFMA" in m and m["SQ_INSTS_MFMA"] > 0:
+        r = 1.0 / m["SQ_INSTS_MFMA"]
+        parts = [f"{k[9:]} {m[k] * r:.2f}" for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD") if k in m]
+        print("instructions per MFMA instruction (SQ_INSTS_VALU counts the MFMA and transcendental "
+              "instructions too): " + ", ".join(parts))
+
+
+def _rows_all(path):
+    return list(csv.DictReader(open(path)))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -124,11 +176,17 @@ def main():
     p.add_argument("--phases", type=int, required=True)
     p.add_argument("--fetch-factor", type=float, required=True)
     p.add_argument("--write-factor", type=float, required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csvs", nargs="+", help="counter_collection.csv of each pass")
+    c.add_argument("--phases", type=int, required=True)
+    c.add_argument("--label", default="extend phase 1", help="dispatch class prefix to average")
     a = ap.parse_args()
     if a.cmd == "trace":
         trace(a.csv, a.phases, a.runs)
-    else:
+    elif a.cmd == "pmc":
         pmc(a.fetch_csv, a.write_csv, a.phases, a.fetch_factor, a.write_factor)
+    else:
+        counters(a.csvs, a.phases, a.label)
 
 
 if __name__ == "__main__":
