@@ -15,7 +15,7 @@ from .runtime import Runtime
 
 class WorkloadRun:
     def __init__(self, wl, device="cuda", extend_items: int = 0, decode_items: int = 0, extra_slots: int = 0,
-                 hole_seed: int | None = None):
+                 hole_seed: int | None = None, kv_row_pitch: int | None = None):
         import torch
 
         self.torch = torch
@@ -26,7 +26,7 @@ class WorkloadRun:
         self.hole_seed = hole_seed
         max_rows = max(len(ph.requests) for ph in wl.phases)
         self.rt = Runtime(cfg.dtype, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, self.num_slots, max_rows,
-                          cfg.max_seq_len, device, extend_items, decode_items)
+                          cfg.max_seq_len, device, extend_items, decode_items, kv_row_pitch)
         tdt = self.rt.tdtype
         dev = self.rt.device
         self.inputs = []

@@ -108,7 +108,8 @@ class Request:
 
 class Runtime:
     def __init__(self, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int, num_slots: int,
-                 max_rows: int, ld: int, device="cuda", extend_items: int = 0, decode_items: int = 0):
+                 max_rows: int, ld: int, device="cuda", extend_items: int = 0, decode_items: int = 0,
+                 kv_row_pitch: int | None = None):
         import torch
 
         self.torch = torch
@@ -120,9 +121,12 @@ class Runtime:
         self.desc = rdx.attn_desc(rdx.BF16 if dtype == "bf16" else rdx.F32, num_q_heads, num_kv_heads,
                                   head_dim, num_slots)
         # pools with the row pitch the kernels stream fastest (rows padded past
-        # the Hkv x head_dim a slot holds)
-        self.kv_row_pitch = rdx.kv_row_pitch_recommended(self.desc)
-        self.desc.kv_row_pitch = self.kv_row_pitch
+        # the Hkv x head_dim a slot holds), unless the caller gives one
+        # (elements; 0 = dense rows)
+        if kv_row_pitch is None:
+            kv_row_pitch = rdx.kv_row_pitch_recommended(self.desc)
+        self.desc.kv_row_pitch = kv_row_pitch
+        self.kv_row_pitch = kv_row_pitch or num_kv_heads * head_dim
         self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_dim
         self.num_slots, self.ld, self.max_rows = num_slots, ld, max_rows
         self.tree = rdx.Tree(num_slots)

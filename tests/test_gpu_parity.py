@@ -31,7 +31,7 @@ def _fragmenter(num_slots, keep, seed):
 
 
 def run_and_check(cfg, sample_leaves=None, extend_items=0, decode_items=0, hole_seed=None, extra_slots=0,
-                  poison=False, leaf_extra=()):
+                  poison=False, leaf_extra=(), kv_row_pitch=None):
     """poison: every pool row starts as NaN, so any key or value the kernels
     read that the workload never wrote shows up in the outputs.
     leaf_extra: rids checked besides the sampled leaves (other phases)."""
@@ -42,7 +42,7 @@ def run_and_check(cfg, sample_leaves=None, extend_items=0, decode_items=0, hole_
     print(f"\n[gpu] {cfg.name} levels={cfg.levels} Hq/Hkv={cfg.n_q_heads}/{cfg.n_kv_heads} D={cfg.head_dim} "
           f"{cfg.dtype} items={extend_items}/{decode_items} holes={hole_seed}", flush=True)
     run = WorkloadRun(wl, extend_items=extend_items, decode_items=decode_items, hole_seed=hole_seed,
-                      extra_slots=extra_slots)
+                      extra_slots=extra_slots, kv_row_pitch=kv_row_pitch)
     if poison:
         run.rt.k_pool.fill_(float("nan"))
         run.rt.v_pool.fill_(float("nan"))
@@ -230,3 +230,21 @@ def test_decode_long_items():
     row_bytes = 8 * 128 * 2
     extra = (1 << 31) // row_bytes + 4096
     run_and_check(cfg, decode_items=8, hole_seed=3, extra_slots=extra, poison=True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("pitch_pad", [0, 8])
+@pytest.mark.parametrize("name,levels,decode", [
+    ("batchllm", ((3, 150), (5, 70)), 3),
+    ("tiny", ((1, 64), (4, 16)), 3),
+])
+def test_kv_row_pitch(name, levels, decode, pitch_pad):
+    """The pools' row pitch is the caller's: dense rows (kv_row_pitch 0) and
+    rows padded by 16 bytes (8 bf16 / 4 fp32 elements past Hkv x head_dim)
+    give the oracle's outputs through the store, extend (both split modes)
+    and decode kernels, with unwritten pool memory poisoned."""
+    cfg = config_by_name(name).replace(levels=levels, decode_steps=decode)
+    elems = 0 if pitch_pad == 0 else cfg.n_kv_heads * cfg.head_dim + (pitch_pad if cfg.dtype == "bf16" else 4)
+    for items in (0, 100000):
+        run, _, _ = run_and_check(cfg, extend_items=items, decode_items=items, poison=True, kv_row_pitch=elems)
+        assert run.rt.kv_row_pitch == (elems or cfg.n_kv_heads * cfg.head_dim)
