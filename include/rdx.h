@@ -274,12 +274,21 @@ typedef struct rdx_attn_desc {
 int rdx_kv_row_pitch_recommended(const rdx_attn_desc* desc, int32_t* out);
 
 /* Scatter new K/V rows into the pools: pool[slots[i]] = new[i], i < n.
- * slots: device int32[n], distinct.  Errors: EINVAL, EUNSUPPORTED, EDEVICE. */
+ * The pages only say that each token's KV lives in GPU pages that requests
+ * share (SGLang paper notes, section 3); this is the plumbing that puts it
+ * there.  slots: device int32[n], distinct.  Errors: EINVAL, EUNSUPPORTED,
+ * EDEVICE. */
 int rdx_kv_store(const rdx_attn_desc* desc, void* k_pool, void* v_pool,
                  const void* k_new, const void* v_new, const int32_t* slots,
                  int64_t n, void* stream);
 
 /* ------------------------------------------------------------------ plan */
+/* The work list of one attention launch.  Its structure is this library's:
+ * the BatchLLM explainer (Horizontal Fusion) has the shared-prefix part and
+ * each request's distinct part computed by different workgroups of one
+ * kernel and their partial results combined; here a part is a job (a key
+ * range of one page-table row for a token range of a row tile), and a tile
+ * whose key ranges are split across workgroups is combined by the merge. */
 typedef struct rdx_plan rdx_plan;
 #define RDX_PLAN_EXTEND 0
 #define RDX_PLAN_DECODE 1
