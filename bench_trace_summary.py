@@ -16,6 +16,7 @@ before it.
     python3 bench_trace_summary.py pmc <FETCH run_counter_collection.csv> <WRITE ...csv> --phases N \\
         --fetch-factor F --write-factor W
     python3 bench_trace_summary.py counters <pass1 csv> <pass2 csv> ... --phases N [--label "extend phase 1"]
+    python3 bench_trace_summary.py gaps <run_kernel_trace.csv> --phases N
 """
 from __future__ import annotations
 
@@ -159,6 +160,52 @@ def counters(paths, n_phases, label_prefix):
               "instructions too): " + ", ".join(parts))
 
 
+def gaps(path, n_phases, top=12):
+    """Idle time of the GPU in the last pass of the workload: from the first
+    dispatch after the previous pass's last decode step to the run's last
+    dispatch, the span, the time some kernel ran (union of the dispatch
+    intervals) and the gaps between consecutive dispatches, summed by the
+    classes on either side and listed largest first."""
+    rows = _rows(path)
+    labels = classify([r["Kernel_Name"] for r in rows], n_phases)
+    hint0 = [i for i, l in enumerate(labels) if l.startswith("extend phase 0")]
+    if not hint0:
+        raise SystemExit("no extend phase 0 dispatch in the trace")
+    start = 0
+    for i in range(hint0[-1] - 1, -1, -1):
+        if labels[i].startswith("decode") or labels[i] == "merge after decode":
+            start = i + 1
+            break
+    win = [(int(rows[i]["Start_Timestamp"]), int(rows[i]["End_Timestamp"]), labels[i]) for i in range(start, len(rows))]
+    win.sort()
+    span = win[-1][1] - win[0][0]
+    busy, cur_s, cur_e = 0, win[0][0], win[0][1]
+    gl = []
+    for (s0, e0, l0), (s1, e1, l1) in zip(win, win[1:]):
+        if s1 > cur_e:
+            busy += cur_e - cur_s
+            gl.append((s1 - cur_e, l0, l1))
+            cur_s, cur_e = s1, e1
+        else:
+            cur_e = max(cur_e, e1)
+    busy += cur_e - cur_s
+    print(f"last pass: {len(win)} dispatches, span {span / 1e3:.1f} us, kernels running {busy / 1e3:.1f} us, "
+          f"idle {(span - busy) / 1e3:.1f} us in {len(gl)} gaps")
+    by = collections.defaultdict(lambda: [0, 0])
+    for g, l0, l1 in gl:
+        k = (l0.split(": ")[0], l1.split(": ")[0])
+        by[k][0] += 1
+        by[k][1] += g
+    print()
+    print("| previous dispatch | next dispatch | gaps | total (us) | mean (us) |")
+    print("|---|---|---:|---:|---:|")
+    for (a, b), (n, t) in sorted(by.items(), key=lambda x: -x[1][1])[:top]:
+        print(f"| `{a}` | `{b}` | {n} | {t / 1e3:.1f} | {t / 1e3 / n:.2f} |")
+    print()
+    print("largest gaps (us): " + ", ".join(f"{g / 1e3:.1f} ({l0.split(': ')[0]} -> {l1.split(': ')[0]})"
+                                            for g, l0, l1 in sorted(gl, reverse=True)[:top]))
+
+
 def _rows_all(path):
     return list(csv.DictReader(open(path)))
 
@@ -180,9 +227,14 @@ def main():
     c.add_argument("csvs", nargs="+", help="counter_collection.csv of each pass")
     c.add_argument("--phases", type=int, required=True)
     c.add_argument("--label", default="extend phase 1", help="dispatch class prefix to average")
+    g = sub.add_parser("gaps")
+    g.add_argument("csv")
+    g.add_argument("--phases", type=int, required=True)
     a = ap.parse_args()
     if a.cmd == "trace":
         trace(a.csv, a.phases, a.runs)
+    elif a.cmd == "gaps":
+        gaps(a.csv, a.phases)
     elif a.cmd == "pmc":
         pmc(a.fetch_csv, a.write_csv, a.phases, a.fetch_factor, a.write_factor)
     else:

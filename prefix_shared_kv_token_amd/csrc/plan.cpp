@@ -206,15 +206,35 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
   tiles.clear();
   sc.trs.clear();
   sc.tile_tr_begin.clear();
-  int64_t cur_key = INT64_MIN;
-  for (int r : order) {
+  int64_t cur_key = INT64_MIN, cur_key2 = INT64_MIN;
+  // decode tiles hold one top-level sharing group; inside it, a run of
+  // requests that also share their next segment (a branch of the tree) starts
+  // a fresh tile when it would not fit in the current one but fits in a
+  // tile of its own, so that no branch is streamed by two tiles
+  auto key2_of = [&](const Req& q) -> int64_t { return q.seg_len < 2 ? -1 : sb[q.seg_off + 1]; };
+  for (int oi = 0; oi < R; ++oi) {
+    const int r = order[oi];
     const Req& q = rq[r];
     if (q.q_len == 0) continue;
-    int64_t key;
-    if (kind == RDX_PLAN_EXTEND)
+    int64_t key, key2 = -1;
+    if (kind == RDX_PLAN_EXTEND) {
       key = q.seg_len == 0 ? -1 - (int64_t)r : sb[q.seg_off + q.seg_len - 1];
-    else
+    } else {
       key = q.seg_len == 0 ? -1 : sb[q.seg_off];
+      key2 = key2_of(q);
+      const int ntile = (int)sc.tile_tr_begin.size();
+      if (key2 >= 0 && ntile > 0 && key == cur_key && key2 != cur_key2) {
+        int64_t run = 0;
+        for (int oj = oi; oj < R; ++oj) {
+          const Req& x = rq[order[oj]];
+          if (x.seg_len < 1 || sb[x.seg_off] != key || key2_of(x) != key2) break;
+          run += x.q_len;
+        }
+        const int used = tiles[(ntile - 1) * kTileWords + 1];
+        if (used > 0 && used + run > tt && run <= tt) cur_key = INT64_MIN;  // forces a fresh tile
+      }
+      cur_key2 = key2;
+    }
     for (int t = 0; t < q.q_len; ++t) {
       int ntile = (int)sc.tile_tr_begin.size();
       bool fresh = ntile == 0 || key != cur_key || tiles[(ntile - 1) * kTileWords + 1] >= tt;

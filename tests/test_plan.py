@@ -261,13 +261,14 @@ def test_default_decode_launch_size(name, items):
 def test_multilevel_decode_tiles():
     """Multi-level tree (root 1,024 -> 8 branches of 512 -> 3 forks of 128;
     GQA 32/8), first decode step: 24 leaves x 4 grouped heads = 96 rows in
-    64-row decode tiles -- 16 leaves, then 8.  The root is a job of both
-    tiles and branch 5 (leaves 15-17) straddles them, so the plan issues
-    1,024 x 2 + 512 x 9 = 6,656 shared key reads per KV head for 5,120
-    distinct shared keys.  Both tiles' items for a KV head run on the same
-    XCD, and the counters show the second read is served from its L2: the
-    kernel's HBM reads per launch equal the algorithmic bytes (tiles of up
-    to 128 rows, measured, read no fewer HBM bytes and ran slower)."""
+    64-row decode tiles.  Tiles are cut on branch boundaries: branches 0-4
+    (15 leaves, 60 rows), then 5-7 (9 leaves, 36 rows), so every branch is a
+    job of exactly one tile and only the root, whose 96 rows cannot share one
+    tile, is read by both: 1,024 x 2 + 512 x 8 = 6,144 shared key reads per
+    KV head for 5,120 distinct shared keys.  Both tiles' items for a KV head
+    run on the same XCD, and the counters show the root's second read is
+    served from its L2 (tiles of up to 128 rows, measured, read no fewer HBM
+    bytes and ran slower)."""
     cfg = config_by_name("multilevel")
     wl, tree, phases = _admit_phases(cfg)
     reqs = phases[-1]
@@ -278,11 +279,85 @@ def test_multilevel_decode_tiles():
     plan.build(tree, [n for _, _, n, _ in reqs], rows, kv1, [1] * len(reqs), [len(p) for p, *_ in reqs],
                tree.alloc(len(reqs)), cfg.max_seq_len)
     v = _check_coverage(plan, kv1, [1] * len(reqs), rows, cfg.n_kv_heads)
-    assert [int(t[1]) * 4 for t in v["tiles"]] == [64, 32]
+    assert [int(t[1]) * 4 for t in v["tiles"]] == [60, 36]
     shared = sum(int(j[2] - j[1]) for j in v["jobs"] if j[5] == 0)
     own = sum(int(j[2] - j[1]) for j in v["jobs"] if j[5] == 1)
-    assert shared == 1024 * 2 + 512 * 9
+    assert shared == 1024 * 2 + 512 * 8
     assert own == 24 * (128 + 1)
+    # each shared segment's tiles: the root in both, each branch in one
+    tiles_of = {}
+    for it in v["items"]:
+        for jx in range(int(it[1]), int(it[2])):
+            j = v["jobs"][jx]
+            if j[5] == 0:
+                tiles_of.setdefault((int(j[1]), int(j[2]), int(j[0]) if j[1] > 0 else -1), set()).add(int(it[0]))
+    root = [t for (k0, k1, _), t in tiles_of.items() if (k0, k1) == (0, 1024)]
+    branches = [t for (k0, k1, _), t in tiles_of.items() if (k0, k1) == (1024, 1536)]
+    assert root == [{0, 1}]
+    assert len(branches) == 8 and all(len(t) == 1 for t in branches)
+
+
+def test_decode_tiles_cut_on_branch_boundaries():
+    """Random two-level groups (a root shared by every request of the group,
+    branches shared by runs of them): a branch whose requests fit in one
+    decode tile is a job of one tile only, and a tile ends before it is full
+    only where the next branch's requests would not fit in it."""
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        nb = int(rng.integers(2, 9))
+        sizes = [int(x) for x in rng.integers(1, 22, nb)]
+        root = [int(x) for x in rng.integers(1, 30000, 100)]
+        tree = rdx.Tree(200000)
+        prompts = []
+        for b, n in enumerate(sizes):
+            br = [30001 + b] + [int(x) for x in rng.integers(1, 30000, 40)]
+            for i in range(n):
+                prompts.append(root + br + [31000 + 100 * b + i] + [int(x) for x in rng.integers(1, 30000, 5)])
+        nodes = []
+        for p in prompts:
+            m, slots, node = tree.match_prefix(p)
+            new = tree.alloc(len(p) - m)
+            node = tree.insert(p, np.concatenate([slots, new]).astype(np.int32))
+            nodes.append(node)
+        reqs = []
+        for p in prompts:
+            m, slots, node = tree.match_prefix(p)
+            assert m == len(p)
+            tree.lock(node)
+            reqs.append((p, node))
+        hq, hkv = 8, 2   # 4 rows per request: 16 requests per 64-row decode tile
+        desc = rdx.attn_desc(rdx.BF16, hq, hkv, 128, 200000)
+        plan = rdx.Plan(desc, rdx.PLAN_DECODE, 8)
+        kv1 = [len(p) + 1 for p, _ in reqs]
+        rows = list(range(len(reqs)))
+        plan.build(tree, [n for _, n in reqs], rows, kv1, [1] * len(reqs), [len(p) for p, _ in reqs],
+                   tree.alloc(len(reqs)), 256)
+        v = _check_coverage(plan, kv1, [1] * len(reqs), rows, hkv)
+        tiles_of = {}
+        for it in v["items"]:
+            for jx in range(int(it[1]), int(it[2])):
+                j = v["jobs"][jx]
+                if j[5] == 0 and int(j[1]) == 100:   # a branch segment: keys 100 .. 141
+                    tiles_of.setdefault(int(j[0]), set()).add(int(it[0]))
+        # a branch's job reads the page-table row of its first request
+        first_row = {int(sum(sizes[:b])): b for b in range(nb) if sizes[b] >= 2}
+        assert set(tiles_of) == set(first_row), (sizes, tiles_of)
+        for row, b in first_row.items():
+            if sizes[b] <= 16:
+                assert len(tiles_of[row]) == 1, (sizes, b, tiles_of[row])
+            else:   # larger than a tile: consecutive tiles, no more than needed plus one
+                t = sorted(tiles_of[row])
+                assert t == list(range(t[0], t[-1] + 1)) and len(t) <= -(-sizes[b] // 16) + 1, (sizes, b, t)
+        branch_of = [b for b, n in enumerate(sizes) for _ in range(n)]
+        toks = v["tokens"]
+        tiles = v["tiles"]
+        for t in range(len(tiles) - 1):
+            n_tok = int(tiles[t][1])
+            if n_tok == 16:
+                continue
+            nxt = [branch_of[int(toks[int(tiles[t + 1][0]) + i][0])] for i in range(int(tiles[t + 1][1]))]
+            first = sum(1 for b in nxt if b == nxt[0])
+            assert n_tok + first > 16, (sizes, t, n_tok, first)
 
 
 @pytest.mark.parametrize("group", [1, 4])
