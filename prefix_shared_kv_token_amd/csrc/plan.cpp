@@ -189,11 +189,13 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
     const Node* const* path = sc.path_buf.data() + q.path_off;
     for (int k = 0; k < q.path_len; ++k) {
       const Node* n = path[k];
-      for (int64_t p = std::max<int64_t>(n->start, q.written); p < n->end(); ++p)
-        run_slots.push_back(n->slots[p - n->start]);
+      const int64_t p0 = std::max<int64_t>(n->start, q.written);
+      if (p0 < n->end())
+        run_slots.insert(run_slots.end(), n->slots.begin() + (p0 - n->start), n->slots.begin() + (n->end() - n->start));
     }
-    for (int64_t i = std::max<int64_t>(0, (int64_t)q.written - (q.kv_len - q.q_len)); i < q.q_len; ++i)
-      run_slots.push_back(b.new_slots[q.new_off + i]);
+    const int64_t i0 = std::max<int64_t>(0, (int64_t)q.written - (q.kv_len - q.q_len));
+    if (i0 < q.q_len)
+      run_slots.insert(run_slots.end(), b.new_slots + q.new_off + i0, b.new_slots + q.new_off + q.q_len);
     int64_t count = (int64_t)run_slots.size() - src;
     if (count != q.kv_len - q.written) return fail(RDX_EINVAL, "rdx_plan_build: request %d: page-table gap", r);
     runs.insert(runs.end(), {q.row, q.written, (int32_t)count, (int32_t)src});
@@ -235,7 +237,8 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
       }
       cur_key2 = key2;
     }
-    for (int t = 0; t < q.q_len; ++t) {
+    // the request's tokens in runs that fill the current tile
+    for (int t = 0; t < q.q_len;) {
       int ntile = (int)sc.tile_tr_begin.size();
       bool fresh = ntile == 0 || key != cur_key || tiles[(ntile - 1) * kTileWords + 1] >= tt;
       if (fresh) {
@@ -245,13 +248,21 @@ int Plan::build(const RadixTree& tree, const rdx_batch& b, int64_t page_ld) {
         ntile++;
       }
       int32_t* tl = &tiles[(ntile - 1) * kTileWords];
-      int local = tl[1];
+      const int local = tl[1];
+      const int n = std::min(q.q_len - t, tt - local);
       if ((int)sc.trs.size() == sc.tile_tr_begin.back() || sc.trs.back().r != r) sc.trs.push_back({r, local, local, 0});
-      sc.trs.back().hi = local + 1;
-      sc.trs.back().pmax = q.kv_len - q.q_len + t;
-      tl[1]++;
-      toks.push_back(q.q_off + t);
-      toks.push_back(q.kv_len - q.q_len + t);
+      sc.trs.back().hi = local + n;
+      sc.trs.back().pmax = q.kv_len - q.q_len + t + n - 1;
+      tl[1] += n;
+      const size_t at = toks.size();
+      toks.resize(at + (size_t)n * kTokWords);
+      int32_t* out = toks.data() + at;
+      const int32_t qi = q.q_off + t, pos = q.kv_len - q.q_len + t;
+      for (int i = 0; i < n; ++i) {
+        out[2 * i] = qi + i;
+        out[2 * i + 1] = pos + i;
+      }
+      t += n;
     }
   }
   const int ntiles = (int)sc.tile_tr_begin.size();
