@@ -436,7 +436,7 @@ def eviction_probe(rdx, pools=(4000, 6000, 10000)):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="batchllm",
                     help="headline workload (default: the largest, BatchLLM micro shape)")
