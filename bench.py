@@ -458,6 +458,8 @@ def main():
                     help="run the job's iterations from Python (default: rdx_job_* in the library)")
     ap.add_argument("--m-threshold", type=int, default=0,
                     help="KV memory bound in K/V entries (default: a fifth of the job's)")
+    ap.add_argument("--extra-slots", type=int, default=0,
+                    help="pool slots beyond the workload's tokens (a pool over 2 GiB runs the 64-bit offset kernels)")
     ap.add_argument("--extend-items", type=int, default=0)
     ap.add_argument("--decode-items", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -557,7 +559,8 @@ def measure_workload(args, cfg, wl, steps: int, warmup: int, instrumented: int) 
     print(f"[bench] {cfg.name}: building inputs", file=sys.stderr, flush=True)
     shuffled = args.shuffle_seed is not None
     run = WorkloadRun(wl, extend_items=args.extend_items, decode_items=args.decode_items,
-                      hole_seed=args.shuffle_seed, extra_slots=cfg.total_tokens() if shuffled else 0)
+                      hole_seed=args.shuffle_seed,
+                      extra_slots=(cfg.total_tokens() if shuffled else 0) + args.extra_slots)
     # long-lived objects (inputs, torch, the workload) out of the collector's
     # reach, as a serving process does after start-up: a full collection of
     # them would otherwise land inside some step
@@ -653,8 +656,10 @@ def measure_workload(args, cfg, wl, steps: int, warmup: int, instrumented: int) 
         "config": {"workload": cfg.name, "levels": [list(l) for l in cfg.levels],
                    "decode_steps": cfg.decode_steps, "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "tokens_per_step": tokens_per_step, "parallelism": "none (1 GPU)",
-                   "pool": (f"scattered: 2x slots, random half free (seed {args.shuffle_seed})" if shuffled
-                            else "exact size, ascending free ids")},
+                   "pool": ((f"scattered: 2x slots, random half free (seed {args.shuffle_seed})" if shuffled
+                             else "exact size, ascending free ids")
+                            + (f", {args.extra_slots} extra slots" if args.extra_slots else "")),
+                   "pool_bytes_per_matrix": run.rt.k_pool.numel() * run.rt.k_pool.element_size()},
         "extend_query_tokens_per_s": member_tokens / ext_member_s,
         "decode_tokens_per_s": cfg.decode_steps * R / dec_total_s if dec_total_s else None,
         "roofline": dominant,

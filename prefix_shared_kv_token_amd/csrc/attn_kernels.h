@@ -723,9 +723,11 @@ struct DecPool {
         const int64_t off = (int64_t)(none ? 0u : o) * row_bytes + in_row + 16 * i;
         const uint4 x = *reinterpret_cast<const uint4*>(kb + off);
         const uint4 y = *reinterpret_cast<const uint4*>(vb + off);
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        st.k[i] = none ? z : x;
-        st.v[i] = none ? z : y;
+        // zeros by a mask, not a select of the two vectors (which the
+        // compiler lowers through private memory)
+        const uint32_t keep = none ? 0u : ~0u;
+        st.k[i] = make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep);
+        st.v[i] = make_uint4(y.x & keep, y.y & keep, y.z & keep, y.w & keep);
       }
     }
   }
