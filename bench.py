@@ -442,7 +442,7 @@ def main():
                     help="headline workload (default: the largest, BatchLLM micro shape)")
     ap.add_argument("--also", default="helpdesk,longprefix,multilevel",
                     help="other workloads measured after the headline (their fractions as extra keys)")
-    ap.add_argument("--also-steps", type=int, default=3)
+    ap.add_argument("--also-steps", type=int, default=10)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--shuffle-seed", type=int, default=None,
@@ -523,7 +523,7 @@ def main():
                 continue
             ocfg = config_by_name(name)
             print(f"[bench] also {name}", file=sys.stderr, flush=True)
-            om = measure_workload(args, ocfg, Workload(ocfg), args.also_steps, 1, 1)
+            om = measure_workload(args, ocfg, Workload(ocfg), args.also_steps, args.warmup, 1)
             others[name] = {k: om[k] for k in ("value", "ms_per_step", "extend_query_tokens_per_s",
                                                "decode_tokens_per_s", "extend_roofline",
                                                "extend_roofline_hint_plus_member", "hint_extend_roofline",
