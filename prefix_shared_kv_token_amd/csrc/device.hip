@@ -317,12 +317,15 @@ int rdx_plan_upload(rdx_plan* hplan, void* dev_plan, int64_t dev_plan_bytes, int
 void rdx_plan_destroy(rdx_plan* hplan) {
   if (!hplan) return;
   Plan* p = reinterpret_cast<Plan*>(hplan);
+  // teardown has no caller to report to: each buffer is released whatever
+  // the status of the calls before it (a copy still reading a staging
+  // buffer is waited for first)
   for (Plan::Stage& sg : p->stages) {
-    if (sg.pending && sg.event) hipEventSynchronize(reinterpret_cast<hipEvent_t>(sg.event));
-    if (sg.event) hipEventDestroy(reinterpret_cast<hipEvent_t>(sg.event));
-    if (sg.pinned) hipHostFree(sg.pinned);
+    if (sg.pending && sg.event) (void)hipEventSynchronize(reinterpret_cast<hipEvent_t>(sg.event));
+    if (sg.event) (void)hipEventDestroy(reinterpret_cast<hipEvent_t>(sg.event));
+    if (sg.pinned) (void)hipHostFree(sg.pinned);
   }
-  for (void* r : p->retired) hipHostFree(r);
+  for (void* r : p->retired) (void)hipHostFree(r);
   delete p;
 }
 
