@@ -195,8 +195,9 @@ def test_separate_calls_match_decode_step():
 # Helpdesk: extend tiles of 256 rows (6.4 requests), one 64-row decode tile.
 # BatchLLM / Long-prefix: groups of 16 members (a decode tile each); first
 # and last member of several groups.  Multi-level: 24 leaves under 8
-# branches of 3; decode tiles of 64 rows hold 16 leaves, so leaves 15 and 16
-# sit on either side of a tile boundary inside one branch's sharing.
+# branches of 3; decode tiles are cut on branch boundaries (leaves 0-14,
+# then 15-23), so leaves 14 and 15 sit on either side of the tile boundary,
+# and 15-17 share the branch that opens the second tile.
 FULL_SAMPLES = {
     "helpdesk": [0, 6, 7, 31, 32, 63],
     "batchllm": [0, 15, 16, 31, 500, 511, 512, 1008, 1023],
