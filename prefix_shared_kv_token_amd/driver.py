@@ -108,10 +108,8 @@ class WorkloadRun:
                     dec_buf = torch.empty((T, R, cfg.n_q_heads, cfg.head_dim), dtype=rt.tdtype, device=rt.device)
                 else:
                     dec_buf = torch.empty((1, R, cfg.n_q_heads, cfg.head_dim), dtype=rt.tdtype, device=rt.device)
-                for t in range(T):
-                    tm = self._timer(timers, "decode")
-                    rt.decode_step(reqs, self.dq[t], self.dk[t], self.dv[t],
-                                   o=dec_buf[t if keep_outputs else 0], timer=tm)
+                tms = [self._timer(timers, "decode") for _ in range(T)] if timers is not None else None
+                rt.decode_steps(reqs, self.dq, self.dk, self.dv, dec_buf if keep_outputs else dec_buf[0], timers=tms)
                 out["decode"] = dec_buf
             out["matched"].append(reqs.matched.tolist())
             if keep_outputs:

@@ -316,6 +316,60 @@ class Runtime:
             timer[1].record()
         return o
 
+    def decode_steps(self, reqs: Batch, q, k_new, v_new, o, timers=None):
+        """T decode steps back to back, the same calls as T decode_step calls
+        with the tensors checked once: q [T, R, Hq, D], k_new/v_new
+        [T, R, Hkv, D]; o [T, R, Hq, D] (step t writes o[t]) or [R, Hq, D]
+        (every step writes it: it ends holding the last step's output).
+        timers: None, or one event pair per step (then each step goes
+        through decode_step)."""
+        T = q.shape[0] if q.dim() == 4 else -1
+        if T < 0 or k_new.dim() != 4 or v_new.dim() != 4 or k_new.shape[0] != T or v_new.shape[0] != T:
+            raise ValueError("decode_steps: q, k_new, v_new must be [T, R, heads, D] with the same T")
+        per_step_o = o.dim() == 4
+        if per_step_o and o.shape[0] != T:
+            raise ValueError("decode_steps: o must be [T, R, Hq, D] or [R, Hq, D]")
+        if self.record is not None or timers is not None:
+            for t in range(T):
+                self.decode_step(reqs, q[t], k_new[t], v_new[t], o=o[t] if per_step_o else o,
+                                 timer=timers[t] if timers is not None else None)
+            return o
+        if T == 0:
+            return o
+        n = reqs.n
+        # every step's slice is checked through the first one: same shape, and
+        # contiguous when the first is (slices of a tensor along dim 0)
+        self._check_step(q[0], k_new[0], v_new[0], o[0] if per_step_o else o, n)
+        q_step, k_step, v_step = (x.stride(0) * x.element_size() for x in (q, k_new, v_new))
+        o_step = o.stride(0) * o.element_size() if per_step_o else 0
+        q0, k0, v0, o0 = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), o.data_ptr()
+        io = self._io
+        plan = self.plans[rdx.PLAN_DECODE]
+        st = self.torch.cuda.current_stream().cuda_stream
+        L = rdx.lib()
+        call = L.rdx_decode_step
+        args_head = (self.tree.handle, plan.handle, self._desc_ref, n, reqs.node_p, reqs.row_p,
+                     self._rs_p[0], self._rs_p[1], self._host_pt_p, self.max_rows, self.ld, reqs.slots_p,
+                     self._io_ref, st, self._info_ref)
+
+        def bind_buffers():
+            dp, ws = self.dev_plan[rdx.PLAN_DECODE], self.workspace
+            io.dev_plan, io.dev_plan_bytes = dp.data_ptr(), dp.numel()
+            io.workspace, io.workspace_bytes = ws.data_ptr(), ws.numel()
+
+        bind_buffers()
+        for t in range(T):
+            io.q, io.k_new, io.v_new, io.o = q0 + t * q_step, k0 + t * k_step, v0 + t * v_step, o0 + t * o_step
+            rc = call(*args_head)
+            if rc == rdx.ENOBUFS:
+                # buffers too small (nothing changed): grow to the reported sizes and retry
+                self._dev_plan(rdx.PLAN_DECODE, self._info.device_bytes)
+                self._workspace(self._info.workspace_bytes)
+                bind_buffers()
+                rc = call(*args_head)
+            rdx._check(rc)
+        return o
+
     def _check_step(self, q, k_new, v_new, o, n):
         for name, t, heads in (("q", q, self.hq), ("k_new", k_new, self.hkv), ("v_new", v_new, self.hkv),
                                ("o", o, self.hq)):

@@ -171,6 +171,28 @@ def test_pool_over_2gib_uses_64bit_addressing():
     assert run.num_slots * row_bytes > (1 << 31)
 
 
+def test_decode_steps_match_decode_step_calls():
+    """Runtime.decode_steps (the stacked step inputs checked once, pointers
+    advanced per step) gives bit-identical outputs and page-table rows to
+    one decode_step call per step (the path a run with per-step timers
+    takes), with one output per step and with one output buffer rewritten
+    by every step."""
+    torch = _torch()
+    from prefix_shared_kv_token_amd.driver import WorkloadRun
+
+    cfg = config_by_name("multilevel").replace(levels=((1, 90), (2, 40), (3, 13)), decode_steps=5)
+    run = WorkloadRun(Workload(cfg))
+    a = run.run()                    # decode_steps
+    b = run.run(timers={})           # decode_step per step
+    c = run.run(keep_outputs=False)  # decode_steps, one shared output buffer
+    torch.cuda.synchronize()
+    assert torch.equal(a["decode"], b["decode"])
+    assert torch.equal(a["decode"][-1], c["decode"][0])
+    for p, q in zip(a["rows"], b["rows"]):
+        for x, y in zip(p, q):
+            np.testing.assert_array_equal(x, y)
+
+
 def test_separate_calls_match_decode_step():
     """The decode path through the separate entry points (rdx_plan_build,
     rdx_plan_upload, rdx_kv_store, rdx_decode_attention; used when launches
