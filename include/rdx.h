@@ -329,8 +329,13 @@ void rdx_plan_destroy(rdx_plan* plan);
 /* Build the work list of one batch: requests are ordered depth-first by
  * their shared nodes, queries are packed into row tiles, each tile gets the
  * shared segments and per-request own ranges it must attend to, and long key
- * ranges are split into separate work items whose partial softmax states are
- * merged in the same launch.  page_table_ld: row stride of the page table.
+ * ranges are split into separate work items whose partial softmax states a
+ * merge kernel combines, issued by the same attention call right behind it.
+ * Extend tiles group the requests that share their deepest shared segment;
+ * decode tiles group one top-level sharing group, and inside it a run of
+ * requests sharing the next segment down starts a fresh tile when it would
+ * overflow the current one but fits in one of its own (so such a segment is
+ * streamed by one tile).  page_table_ld: row stride of the page table.
  * Errors: EINVAL (inconsistent batch), ESTATE (unknown node). */
 int rdx_plan_build(rdx_plan* plan, const rdx_tree* tree, const rdx_batch* batch,
                    int64_t page_table_ld);
