@@ -242,6 +242,19 @@ def test_full_size_sampled(cfg):
     run_and_check(cfg, sample_leaves=FULL_SAMPLES[cfg.name], leaf_extra=extra)
 
 
+def test_full_size_sampled_pool_over_2gib():
+    """BatchLLM at full size with a pool of more than 2 GiB per matrix, so
+    extend and decode run their 64-bit offset variants (the addressing of any
+    pool sized for a large share of HBM), unused pool rows NaN-poisoned:
+    sampled leaves (first and last members of several groups) against the
+    oracle."""
+    cfg = config_by_name("batchllm")
+    row_bytes = cfg.n_kv_heads * cfg.head_dim * 2 + 256   # the recommended padded pitch
+    extra = (1 << 31) // row_bytes + 4096
+    run, _, _ = run_and_check(cfg, sample_leaves=[0, 15, 16, 511, 512, 1023], extra_slots=extra, poison=True)
+    assert run.rt.k_pool.numel() * run.rt.k_pool.element_size() > (1 << 31)
+
+
 def test_decode_long_items():
     """Decode items of 56+ key blocks (a 3,500-token prefix shared by 4
     requests, one decode item per KV head): every output against the
