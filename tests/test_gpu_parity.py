@@ -118,6 +118,35 @@ def test_edge_shapes(base, kw, items):
     run_and_check(config_by_name(base).replace(**kw), extend_items=items, decode_items=items)
 
 
+def _random_case(seed):
+    """A small seeded workload: 1-3 tree levels of random fan-out and length
+    (one-token levels included), GQA group 1-8, head_dim 64 or 128, bf16 or
+    fp32, 1-5 decode steps, an item target from unsplit to one block per
+    item, and half the time a fragmented pool."""
+    rng = np.random.default_rng(7000 + seed)
+    depth = int(rng.integers(1, 4))
+    levels = []
+    for d in range(depth):
+        n = int(rng.integers(1, 4 if d < depth - 1 else 6))
+        levels.append((n, int(rng.integers(1, 150 if d == 0 else 60))))
+    group = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2]))
+    dtype = str(rng.choice(["bf16", "bf16", "fp32"]))
+    kw = dict(levels=tuple(levels), n_q_heads=group * hkv, n_kv_heads=hkv, head_dim=int(rng.choice([64, 128])),
+              dtype=dtype, sigma=0.5 if dtype == "bf16" else 1.0, decode_steps=int(rng.integers(1, 6)))
+    items = int(rng.choice([0, 0, 3, 100000]))
+    holes = (seed, int(rng.integers(1, 400))) if rng.random() < 0.5 else (None, 0)
+    return kw, items, holes
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_shapes(seed):
+    """Every output of a seeded random workload against the oracle."""
+    kw, items, (hole_seed, extra) = _random_case(seed)
+    run_and_check(config_by_name("tiny").replace(**kw), extend_items=items, decode_items=items,
+                  hole_seed=hole_seed, extra_slots=extra)
+
+
 def test_short_last_round_cut_into_quarters():
     """Member extend of 5 wide tiles per KV head on 4 items per head: the
     fifth tile runs as 4 quarter pieces merged by LSE; the decode tile is
