@@ -59,6 +59,48 @@ def test_mixed_small_every_output(cfg, s_chunk, m, items, native):
     assert err <= TOL[cfg.dtype]
 
 
+def _random_mixed(seed):
+    """A small seeded token-batched job: 1-6 groups of 2-5 members (the job
+    stages its inputs by the workload's groups, and the prefix analysis puts
+    a lone member's group at its own edge), prefix
+    1-300 and distinct 1-60 tokens, 1-6 decode steps, GQA 1-4, head_dim 64
+    or 128, bf16 or fp32, s_chunk 3-256 and M_threshold between 2 s_chunk
+    and the job's whole K/V, and an item target from unsplit to tiny."""
+    rng = np.random.default_rng(9100 + seed)
+    group = int(rng.choice([1, 2, 4]))
+    hkv = int(rng.choice([1, 2]))
+    dtype = str(rng.choice(["bf16", "fp32"]))
+    cfg = Config(f"mixed-rand{seed}", 100 + seed, group * hkv, hkv, int(rng.choice([64, 128])), dtype,
+                 0.5 if dtype == "bf16" else 1.0,
+                 ((int(rng.integers(1, 7)), int(rng.integers(1, 300))), (int(rng.integers(2, 6)), int(rng.integers(1, 60)))),
+                 int(rng.integers(1, 7)))
+    s_chunk = int(rng.integers(3, 257))
+    total = 2 * cfg.total_tokens()
+    m = int(rng.integers(2 * s_chunk, max(2 * s_chunk + 1, total + 1)))
+    return cfg, s_chunk, m, int(rng.choice([0, 0, 16, 100000]))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mixed_random_every_output(seed):
+    """Every output and page-table row of a seeded random token-batched job
+    through the library's job runner, against the oracle."""
+    cfg, s_chunk, m, items = _random_mixed(seed)
+    wl, tlen, run = _run(cfg, s_chunk, m, items)
+    ref = run_mixed(wl, s_chunk, m, tlen)
+    assert run.matched == ref["matched"]
+    for rid, row in ref["rows"].items():
+        np.testing.assert_array_equal(run.rows[rid], row)
+    exp = expected_outputs(wl)
+    req, pos = run.job_sources()
+    start = _token_starts(run)
+    o = run.o.float().cpu().numpy()
+    want = np.stack([exp[int(run.req_rid[r])][p - start[r]] for r, p in zip(req, pos)])
+    err = np.abs(o - want).max()
+    print(f"[gpu] {cfg.levels} s_chunk={s_chunk} M={m}: {len(req)} tokens in {len(run.iterations)} launches, "
+          f"max abs err {err:.3g}", flush=True)
+    assert err <= TOL[cfg.dtype]
+
+
 def test_mixed_under_eviction_every_output():
     """A pool of 300 slots for a job of 660 tokens: admissions evict finished
     requests (the slots of their pages are reused while later launches read
