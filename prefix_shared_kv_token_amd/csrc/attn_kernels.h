@@ -483,7 +483,6 @@ template <int D, bool OFF32>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ KVTile<D> buf[2];
   __shared__ int4 slot_buf[2][16];  // page-table slots of the next two key blocks
-  constexpr int KS = KVTile<D>::KS, VS = KVTile<D>::VS;
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over head_dim
   constexpr int DB = D / 32;      // 32-wide d blocks of the output
   constexpr int CH = D / 8;       // 16-byte chunks per K/V row
@@ -497,8 +496,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   // head_dim 128: every thread loads one K and one V unit; 64: threads
   // 0..127 load K, 128..255 load V (wave-uniform).
   const int tid = threadIdx.x;
-  const bool doK = BOTH || tid < UNITS;
-  const bool doV = BOTH || tid >= UNITS;
+  const bool doK = BOTH || tid < UNITS;  // (otherwise the thread loads V)
   const int uk = tid % UNITS;
   const int uv = BOTH ? tid : tid - UNITS;
   const int qd_k = uk / CH, cc_k = uk % CH;
@@ -842,20 +840,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   const bool row_ok = row < n_rows && tloc >= act_lo && tloc < act_hi;
   const bool wave_live = __ballot(row_ok) != 0;
 
-  // Q (B operand of S^T): Q[row][32 db + 8 g .. +8)
+  // Q (B operand of S^T): Q[row][32 db + 8 g .. +8), loaded in the
+  // prologue after the first K/V requests (below)
   bf16x8 qf[DB];
   int qpos = 0;
-  if (row_ok) {
-    const int32_t* tk = a.toks + (int64_t)(tok_begin + tloc) * kTokWords;
-    qpos = tk[1];
-    const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
-                        ((int64_t)tk[0] * a.hq + (int64_t)kvh * group + row % group) * D + 8 * g;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(src + 32 * db);
-  } else {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) qf[db] = bf16x8{};
-  }
   f32x4 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -869,6 +857,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   // slot of this thread's key in the block the iterator is at (-1: none)
   auto slot_of = [&](const BlockIter& it) { return it.kb + kk < it.k1 ? it.prow[it.kb + kk] : -1; };
 
+  // the lane's token record (caller row, position); rows outside the tile
+  // read their clamped token's: finite Q values whose keys are all masked and
+  // whose results are never written
+  const int tl = max(0, min(tloc, n_tok - 1));
+  int2 tok = make_int2(0, 0);
   if (nblk > 0) {
     BlockIter it_s, it_c;
     it_s.j = jb;
@@ -877,14 +870,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
     it_s.k1 = item[13];
     it_c = it_s;
     DecStage<CPT> r0, r1;
-    const uint32_t o0 = pool.offset(slot_of(it_s), in_row);
+    // Loads retire in order for the wait counter: the page-table slots of
+    // blocks 0-2 first, the token record behind them, then the K/V of blocks
+    // 0 and 1 (which wait for their slots only), and Q last, so no wait on
+    // the way to the first K/V request includes the token record or Q.
+    const int s0 = slot_of(it_s);
     iter_next(a, it_s, je);
-    const uint32_t o1 = pool.offset(nblk > 1 ? slot_of(it_s) : -1, in_row);
+    const int s1 = nblk > 1 ? slot_of(it_s) : -1;
     iter_next(a, it_s, je);
     int slot_next = nblk > 2 ? slot_of(it_s) : -1;  // block 2
     iter_next(a, it_s, je);
-    pool.load(r0, o0, in_row);
-    pool.load(r1, o1, in_row);
+    tok = *reinterpret_cast<const int2*>(a.toks + (int64_t)(tok_begin + tl) * kTokWords);
+    pool.load(r0, pool.offset(s0, in_row), in_row);
+    pool.load(r1, pool.offset(s1, in_row), in_row);
+    qpos = tok.y;
+    {
+      const __bf16* src = reinterpret_cast<const __bf16*>(a.q) +
+                          ((int64_t)tok.x * a.hq + (int64_t)kvh * group + row % group) * D + 8 * g;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) qf[db] = *reinterpret_cast<const bf16x8*>(src + 32 * db);
+    }
     dec_store<D, CPT>(buf[0], r0, kk, cq);
     __syncthreads();
 
@@ -920,6 +925,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
       step(b, r0, r1);
       step(b + 1, r1, r0);
     }
+  } else {
+    tok = *reinterpret_cast<const int2*>(a.toks + (int64_t)(tok_begin + tl) * kTokWords);  // the output row
   }
 
   // ---- result: rows of this lane (4 lane groups share a row) ----
@@ -927,8 +934,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(AttnArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!split) {
     if (row_ok) {
-      const int32_t q_index = a.toks[(int64_t)(tok_begin + tloc) * kTokWords];
-      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)q_index * a.hq + (int64_t)kvh * group + row % group) * D;
+      __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((int64_t)tok.x * a.hq + (int64_t)kvh * group + row % group) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         bf16x4 v;
