@@ -178,13 +178,40 @@ def run_mixed_bench(args, cfg, wl):
     print(json.dumps(line, default=float), flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed:
+    what the compiler sees of it (string and character literals, which these
+    sources do not use for comment-like text, are kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
-    """sha256 over the kernel sources and the planner that shapes their
-    launches; a counter summary taken from other sources does not apply."""
+    """sha256 over the code of the kernel sources and of the planner that
+    shapes their launches (comments and layout excluded); a counter summary
+    taken from other code does not apply."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

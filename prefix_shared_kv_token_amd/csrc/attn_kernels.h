@@ -192,10 +192,11 @@ struct Rows4 {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Reads 16-byte chunks of pool rows.  OFF32: the pool is under 4 GiB and is
+// Reads 16-byte chunks of pool rows.  OFF32: the pool is under 2 GiB and is
 // addressed through a raw buffer resource with 32-bit byte offsets
 // (slot * row_bytes + chunk offset, a 24-bit multiply since such a pool has
-// fewer than 2^24 rows); otherwise 64-bit pointer arithmetic.
+// fewer than 2^24 rows of at least 128 bytes; the offset 2^31 is past its end,
+// so a load there returns zeros); otherwise 64-bit pointer arithmetic.
 template <bool OFF32>
 struct PoolReader {
   __amdgpu_buffer_rsrc_t rsrc;
