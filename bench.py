@@ -540,6 +540,7 @@ def main():
         "extend_roofline_hint_plus_member": m["extend_roofline_hint_plus_member"],
         "hint_extend_roofline": m["hint_extend_roofline"],
         "decode_roofline": m["decode_roofline"],
+        "decode_loop_us_per_step": m["decode_loop_us_per_step"],
     }
     if not args.headline_only:
         # the other bf16 workloads, each from an empty tree with its own
@@ -554,7 +555,7 @@ def main():
             others[name] = {k: om[k] for k in ("value", "ms_per_step", "extend_query_tokens_per_s",
                                                "decode_tokens_per_s", "extend_roofline",
                                                "extend_roofline_hint_plus_member", "hint_extend_roofline",
-                                               "decode_roofline")}
+                                               "decode_roofline", "decode_loop_us_per_step")}
             others[name]["config"] = om["config"]
             del om
             import torch
@@ -604,13 +605,18 @@ def measure_workload(args, cfg, wl, steps: int, warmup: int, instrumented: int) 
     per_run = len(wl.phases) + cfg.decode_steps
     n_launch = n_inst * per_run
     print(f"[bench] {cfg.name}: timing {steps} steps ({n_inst} instrumented)", file=sys.stderr, flush=True)
+    # the passes without event-bound dispatches also time their whole decode
+    # loop (store kernel, attention, merge and the gaps between them) with two
+    # events on the stream
+    loop_events = []
     t0 = time.perf_counter()
     for i in range(steps):
         if i == steps - n_inst:
             rdx.timing_begin(n_launch)
-        run.run(keep_outputs=False)
+        run.run(keep_outputs=False, loop_events=loop_events if i < steps - n_inst else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    loop_us = [e0.elapsed_time(e1) * 1e3 / n for e0, e1, n in loop_events if n]
     attn_ms, merge_ms, kinds = rdx.timing_read(n_launch)
     assert len(attn_ms) == n_launch, (len(attn_ms), n_launch)
     ms_per_step = (t1 - t0) * 1e3 / steps
@@ -694,6 +700,7 @@ def measure_workload(args, cfg, wl, steps: int, warmup: int, instrumented: int) 
         "extend_roofline_hint_plus_member": ab_roof,
         "hint_extend_roofline": hint_roof,
         "decode_roofline": decode_roof,
+        "decode_loop_us_per_step": float(np.mean(loop_us)) if loop_us else None,
     }
 
 

@@ -76,11 +76,13 @@ class WorkloadRun:
         keep_free = np.sort(rng.choice(allslots, self.cfg.total_tokens(), replace=False))
         tree.free(keep_free)
 
-    def run(self, keep_outputs: bool = True, timers: dict | None = None, record: bool = False):
+    def run(self, keep_outputs: bool = True, timers: dict | None = None, record: bool = False,
+            loop_events: list | None = None):
         """One pass of every phase.  keep_outputs=False keeps only the last
         decode step's output and no page-table rows.  record=True keeps each
         attention launch (its own plan and buffers) in out["launches"] for
-        Runtime.replay."""
+        Runtime.replay.  loop_events: a list that gets (start, end, steps),
+        events recorded on the stream around the decode loop."""
         torch = self.torch
         rt = self.rt
         rt.reset()
@@ -109,7 +111,13 @@ class WorkloadRun:
                 else:
                     dec_buf = torch.empty((1, R, cfg.n_q_heads, cfg.head_dim), dtype=rt.tdtype, device=rt.device)
                 tms = [self._timer(timers, "decode") for _ in range(T)] if timers is not None else None
+                if loop_events is not None:
+                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    ev[0].record()
                 rt.decode_steps(reqs, self.dq, self.dk, self.dv, dec_buf if keep_outputs else dec_buf[0], timers=tms)
+                if loop_events is not None:
+                    ev[1].record()
+                    loop_events.append((ev[0], ev[1], T))
                 out["decode"] = dec_buf
             out["matched"].append(reqs.matched.tolist())
             if keep_outputs:
