@@ -531,7 +531,11 @@ int rdx_job_launch(rdx_job* job, const rdx_attn_desc* desc, const rdx_step_io* i
  * kernel's (0 when none ran) to out_merge_ms (may be NULL) and the kind
  * (RDX_PLAN_EXTEND / RDX_PLAN_DECODE) to out_kind; it sets *out_n and stops
  * recording.  The recording is process-wide (launches from every thread and
- * plan count); one recording at a time.  Errors: EINVAL, EDEVICE. */
+ * plan count); one recording at a time.  rdx_timing_begin creates the
+ * events for all cap launches itself (events persist for the process), so
+ * the recorded launches create none: a caller that calls it once, and reads
+ * with rdx_timing_read, before a timed region keeps event creation out of
+ * that region.  Errors: EINVAL, EDEVICE. */
 int rdx_timing_begin(int32_t cap);
 int rdx_timing_read(float* out_attn_ms, float* out_merge_ms, int32_t* out_kind, int32_t cap,
                     int32_t* out_n);

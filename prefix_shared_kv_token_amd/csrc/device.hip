@@ -512,6 +512,19 @@ int rdx_decode_step(rdx_tree* tree, rdx_plan* hplan, const rdx_attn_desc* desc, 
 
 int rdx_timing_begin(int32_t cap) {
   if (cap < 0) return fail(RDX_EINVAL, "rdx_timing_begin: negative capacity");
+  // every event the recording can need is created here, so the launches it
+  // records create none (event creation costs the host microseconds per
+  // event, which a host-paced launch sequence would otherwise absorb)
+  while ((int32_t)g_timing.kind.size() < cap) {
+    for (int k = 0; k < 4; ++k) {
+      hipEvent_t x;
+      hipError_t e = hipEventCreate(&x);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      g_timing.ev.push_back(x);
+    }
+    g_timing.kind.push_back(0);
+    g_timing.has_merge.push_back(0);
+  }
   g_timing.on = true;
   g_timing.cap = cap;
   g_timing.used = 0;
