@@ -154,3 +154,13 @@ int main(void) {
     # one group with prefix [1, 2]: 2 + 1 + 1 processed tokens; the batcher
     # emits prefix, 2 distinct chunks and 2 decode tokens
     assert r.stdout.split() == ["1", "4", "5"]
+
+
+def test_timing_errors():
+    """Launch timing rejects a negative capacity and bad read arguments
+    before any device call."""
+    assert rdx.lib().rdx_timing_begin(-1) == rdx.EINVAL
+    n = rdx.i32()
+    assert rdx.lib().rdx_timing_read(None, None, None, -1, rdx.ctypes.byref(n)) == rdx.EINVAL
+    assert rdx.lib().rdx_timing_read(None, None, None, 4, rdx.ctypes.byref(n)) == rdx.EINVAL
+    assert rdx.lib().rdx_timing_read(None, None, None, 0, None) == rdx.EINVAL
