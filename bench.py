@@ -496,7 +496,7 @@ def main():
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU; multi-GPU runs are not part of it "
+        print("bench.py: the benchmark runs on one GPU only; several GPUs are not supported "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
