@@ -6,7 +6,7 @@ HIP code.  Run the CPU test suite against it with
 
     python prefix_shared_kv_token_amd/sanitize/build_host_san.py
     RDX_LIB=prefix_shared_kv_token_amd/sanitize/librdx_host_san.so \\
-    LD_PRELOAD=$(g++ -print-file-name=libasan.so) \\
+    LD_PRELOAD="$(g++ -print-file-name=libasan.so)${LD_PRELOAD:+:$LD_PRELOAD}" \\
     ASAN_OPTIONS=detect_leaks=0 UBSAN_OPTIONS=halt_on_error=1:print_stacktrace=1 \\
     python -m pytest tests -q -m "not gpu"
 

@@ -47,8 +47,16 @@ int rdx_job_launch(rdx_job*, const rdx_attn_desc*, const rdx_step_io*, void*, rd
   return no_device("rdx_job_launch");
 }
 
-int rdx_timing_begin(int32_t) { return no_device("rdx_timing_begin"); }
+// the timing calls check their arguments first, as the device build does
+int rdx_timing_begin(int32_t cap) {
+  if (cap < 0) return fail(RDX_EINVAL, "rdx_timing_begin: negative capacity");
+  return no_device("rdx_timing_begin");
+}
 
-int rdx_timing_read(float*, float*, int32_t*, int32_t, int32_t*) { return no_device("rdx_timing_read"); }
+int rdx_timing_read(float* out_attn_ms, float*, int32_t* out_kind, int32_t cap, int32_t* out_n) {
+  if (!out_n || cap < 0 || (cap > 0 && (!out_attn_ms || !out_kind)))
+    return fail(RDX_EINVAL, "rdx_timing_read: bad arguments");
+  return no_device("rdx_timing_read");
+}
 
 }  // extern "C"
