@@ -1,0 +1,132 @@
+"""Degenerate cases of prefix caching on the GPU, through the runtime and
+the C ABI, against the oracle's cache model and fp64 attention:
+
+* a prompt that is entirely cached (no extend query token of its own: its
+  first new token is a decode token over the cached pages) next to a request
+  that extends the same cached prompt and one that shares nothing;
+* a batch whose prompts are all cached (an extend launch with no query
+  token: no kernel runs);
+* empty batches (no request) through admission, extend, the decode step and
+  finish.
+
+Matched lengths and page-table rows are compared bit for bit, outputs
+within the bf16 tolerance (SGLang explainer, RadixAttention section: a
+cached prefix is reused whole; SGLang paper notes, section 3: reuse leaves
+every token's attention unchanged)."""
+import numpy as np
+import pytest
+
+from oracle import TokenTrieCache, causal_attention
+from workloads.gen import bf16_bits_to_f32, bf16_round_bits
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV, D, SIGMA, T = 8, 2, 128, 0.5, 3
+TOL = 2e-2
+POOL = 2048
+
+
+def _bf16(x):
+    return bf16_bits_to_f32(bf16_round_bits(np.asarray(x, np.float32)))
+
+
+def test_fully_cached_prompts_and_empty_batches():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from prefix_shared_kv_token_amd.runtime import Runtime
+
+    rng = np.random.default_rng(4242)
+    P = rng.integers(0, 32000, 300).astype(np.int32)
+    E = rng.integers(0, 32000, 50).astype(np.int32)
+    U = rng.integers(0, 32000, 120).astype(np.int32)
+    while U[0] == P[0]:
+        U[0] = rng.integers(0, 32000)
+    # logical K/V per token of each sequence (P's shared by everything that starts with it)
+    kv = lambda n: (_bf16(rng.normal(0, SIGMA, (n, HKV, D))), _bf16(rng.normal(0, SIGMA, (n, HKV, D))))
+    kP, vP = kv(len(P))
+    kE, vE = kv(len(E))
+    kU, vU = kv(len(U))
+    dev = torch.device("cuda")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev, torch.bfloat16)
+    rt = Runtime("bf16", HQ, HKV, D, POOL, 8, 1024, "cuda")
+    cache = TokenTrieCache(POOL)
+    print("\n[gpu] edges: fully cached prompt, all-cached batch, empty batches", flush=True)
+
+    # ---- phase 1: P from an empty tree ----
+    qP = _bf16(rng.normal(0, SIGMA, (len(P), HQ, D)))
+    b1 = rt.admit([P])
+    assert b1.matched.tolist() == [0]
+    o1 = rt.extend(b1, t(qP), t(kP), t(vP))
+    m, _, node = cache.match_prefix(P)
+    cache.lock(node)
+    row1 = cache.alloc(len(P))
+    np.testing.assert_array_equal(rt.host_pt[b1.rows[0], :len(P)], row1)
+    ref = causal_attention(qP, kP, vP, np.arange(len(P)))
+    assert np.abs(o1.float().cpu().numpy() - ref).max() <= TOL
+    rt.finish(b1)
+    k_, _ = cache.insert(P, row1)
+    cache.free(row1[m:k_])
+    cache.unlock(node)
+
+    # ---- empty batch through every step ----
+    b0 = rt.admit([])
+    z = lambda h: torch.empty((0, h, D), dtype=torch.bfloat16, device=dev)
+    assert rt.extend(b0, z(HQ), z(HKV), z(HKV)).shape[0] == 0
+    assert rt.decode_step(b0, z(HQ), z(HKV), z(HKV)).shape[0] == 0
+    rt.finish(b0, generated=[])
+    torch.cuda.synchronize()
+
+    # ---- phase 2: P again (all cached), P + E, U ----
+    prompts = [P, np.concatenate([P, E]), U]
+    seq_k = [kP, np.concatenate([kP, kE]), kU]
+    seq_v = [vP, np.concatenate([vP, vE]), vU]
+    b2 = rt.admit(prompts)
+    adm = []
+    for p in prompts:
+        m, slots, node = cache.match_prefix(p)
+        cache.lock(node)
+        adm.append([m, node, list(slots) + cache.alloc(len(p) - m)])
+    assert b2.matched.tolist() == [a[0] for a in adm] == [len(P), len(P), 0]
+    q_new = [_bf16(rng.normal(0, SIGMA, (len(p) - a[0], HQ, D))) for p, a in zip(prompts, adm)]
+    cat = lambda xs: np.concatenate(xs) if xs else np.zeros((0,))
+    o2 = rt.extend(b2, t(cat(q_new)), t(cat([k[a[0]:] for k, a in zip(seq_k, adm)])),
+                   t(cat([v[a[0]:] for v, a in zip(seq_v, adm)])))
+    got = o2.float().cpu().numpy()
+    off = 0
+    for i, (p, a) in enumerate(zip(prompts, adm)):
+        np.testing.assert_array_equal(rt.host_pt[b2.rows[i], :len(p)], a[2])
+        n = len(p) - a[0]
+        if n:
+            ref = causal_attention(q_new[i], seq_k[i], seq_v[i], np.arange(a[0], len(p)))
+            assert np.abs(got[off:off + n] - ref).max() <= TOL, i
+        off += n
+
+    # ---- T decode steps for all three ----
+    gens = [rng.integers(0, 32000, T).astype(np.int32) for _ in prompts]
+    for step in range(T):
+        qd = _bf16(rng.normal(0, SIGMA, (len(prompts), HQ, D)))
+        kd, vd = kv(len(prompts))
+        od = rt.decode_step(b2, t(qd), t(kd), t(vd)).float().cpu().numpy()
+        for i, a in enumerate(adm):
+            a[2] += cache.alloc(1)
+            seq_k[i] = np.concatenate([seq_k[i], kd[i:i + 1]])
+            seq_v[i] = np.concatenate([seq_v[i], vd[i:i + 1]])
+            L = len(seq_k[i])
+            np.testing.assert_array_equal(rt.host_pt[b2.rows[i], :L], a[2])
+            ref = causal_attention(qd[i:i + 1], seq_k[i], seq_v[i], np.array([L - 1]))
+            assert np.abs(od[i:i + 1] - ref).max() <= TOL, (step, i)
+    rt.finish(b2, generated=gens)
+    for p, g, (m, node, row) in zip(prompts, gens, adm):
+        k_, _ = cache.insert(np.concatenate([p, g]), row)
+        cache.free(row[m:k_])
+        cache.unlock(node)
+
+    # ---- phase 3: a batch whose prompts are all cached (no extend query token) ----
+    b3 = rt.admit([P, U])
+    assert b3.matched.tolist() == [len(P), len(U)]
+    o3 = rt.extend(b3, z(HQ), z(HKV), z(HKV))
+    assert o3.shape[0] == 0
+    torch.cuda.synchronize()
+    rt.finish(b3)
+    st = rt.tree.stats()
+    assert st["cached"] == cache.stats()["cached"]
