@@ -7,7 +7,9 @@ the C ABI, against the oracle's cache model and fp64 attention:
 * a batch whose prompts are all cached (an extend launch with no query
   token: no kernel runs);
 * empty batches (no request) through admission, extend, the decode step and
-  finish.
+  finish;
+* a long context: a 40,000-token prompt and a follow-up that reuses it,
+  checked on sampled query positions.
 
 Matched lengths and page-table rows are compared bit for bit, outputs
 within the bf16 tolerance (SGLang explainer, RadixAttention section: a
@@ -130,3 +132,64 @@ def test_fully_cached_prompts_and_empty_batches():
     rt.finish(b3)
     st = rt.tree.stats()
     assert st["cached"] == cache.stats()["cached"]
+
+
+def test_long_context_sampled():
+    """One 40,000-token prompt (causal prefill of 625 row tiles per KV head,
+    items of up to 625 key blocks), then a 1,000-token follow-up that reuses
+    it, then two decode steps; sampled query positions (tile and block
+    boundaries, the ends) against the oracle, page-table rows bit for bit."""
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from prefix_shared_kv_token_amd.runtime import Runtime
+
+    rng = np.random.default_rng(777)
+    L1, L2 = 40000, 1000
+    A = rng.integers(0, 32000, L1).astype(np.int32)
+    B = np.concatenate([A, rng.integers(0, 32000, L2).astype(np.int32)])
+    kv = lambda n: (_bf16(rng.normal(0, SIGMA, (n, HKV, D))), _bf16(rng.normal(0, SIGMA, (n, HKV, D))))
+    kA, vA = kv(L1)
+    kB, vB = kv(L2)
+    dev = torch.device("cuda")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev, torch.bfloat16)
+    pool = L1 + L2 + 16
+    rt = Runtime("bf16", HQ, HKV, D, pool, 4, L1 + L2 + 8, "cuda")
+    cache = TokenTrieCache(pool)
+    print(f"\n[gpu] long context: {L1} + {L2} tokens, Hq/Hkv {HQ}/{HKV}", flush=True)
+
+    qA = _bf16(rng.normal(0, SIGMA, (L1, HQ, D)))
+    b1 = rt.admit([A])
+    o1 = rt.extend(b1, t(qA), t(kA), t(vA)).float().cpu().numpy()
+    m, _, node = cache.match_prefix(A)
+    cache.lock(node)
+    row = cache.alloc(L1)
+    np.testing.assert_array_equal(rt.host_pt[b1.rows[0], :L1], row)
+    pos = np.unique(np.concatenate([[0, 1, 63, 64, 65, 255, 256, L1 // 2, L1 - 65, L1 - 64, L1 - 1],
+                                    rng.integers(0, L1, 24)]))
+    ref = causal_attention(qA[pos], kA, vA, pos)
+    assert np.abs(o1[pos] - ref).max() <= TOL
+    rt.finish(b1)
+    k_, _ = cache.insert(A, row)
+    cache.free(row[m:k_])
+    cache.unlock(node)
+
+    qB = _bf16(rng.normal(0, SIGMA, (L2, HQ, D)))
+    b2 = rt.admit([B])
+    assert b2.matched.tolist() == [L1]
+    o2 = rt.extend(b2, t(qB), t(kB), t(vB)).float().cpu().numpy()
+    m, slots, node = cache.match_prefix(B)
+    assert m == L1
+    cache.lock(node)
+    row = list(slots) + cache.alloc(L2)
+    np.testing.assert_array_equal(rt.host_pt[b2.rows[0], :L1 + L2], row)
+    kF, vF = np.concatenate([kA, kB]), np.concatenate([vA, vB])
+    sel = np.unique(np.concatenate([[0, 63, 64, L2 - 1], rng.integers(0, L2, 12)]))
+    ref = causal_attention(qB[sel], kF, vF, L1 + sel)
+    assert np.abs(o2[sel] - ref).max() <= TOL
+    for step in range(2):
+        qd = _bf16(rng.normal(0, SIGMA, (1, HQ, D)))
+        kd, vd = kv(1)
+        od = rt.decode_step(b2, t(qd), t(kd), t(vd)).float().cpu().numpy()
+        kF, vF = np.concatenate([kF, kd]), np.concatenate([vF, vd])
+        ref = causal_attention(qd, kF, vF, np.array([len(kF) - 1]))
+        assert np.abs(od - ref).max() <= TOL, step
