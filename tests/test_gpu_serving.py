@@ -5,7 +5,8 @@ ordered by rdx_schedule against the tree as it stands (longest shared prefix
 first), then served in batches of 2 through the device path -- admission
 (match, lock, allocate, evicting when short), extend, 4 decode steps,
 finish (insert, free duplicates, unlock) -- on a pool far smaller than the
-queue's tokens, once per eviction policy (LRU, LFU, SLRU, priority).
+queue's tokens, once per eviction policy (LRU, LFU, SLRU, priority), and
+once with LRU and prefix matching in 16-token units.
 
 The same calls run on the oracle's cache model with the oracle's ordering
 (oracle.schedule.lpm_order) and the same policy: the window orders, every
@@ -59,19 +60,24 @@ def _oracle_batch(cache, prompts, gens, batch, prio):
     return {i: (m, np.asarray(row, np.int32)) for i, m, _, row in adm}
 
 
-@pytest.mark.parametrize("policy", ["lru", "lfu", "slru", "priority"])
-def test_scheduled_serving_under_eviction(policy):
+@pytest.mark.parametrize("policy,unit", [("lru", 1), ("lfu", 1), ("slru", 1), ("priority", 1), ("lru", 16)],
+                         ids=["lru", "lfu", "slru", "priority", "lru-unit16"])
+def test_scheduled_serving_under_eviction(policy, unit):
+    """unit 16: matching in whole 16-token blocks (vLLM-vs-SGLang page,
+    matching-unit passage): a cached prefix is reused up to its last whole
+    block, the rest of the prompt is computed again into new slots and
+    freed as a duplicate when the request finishes."""
     import torch
     from prefix_shared_kv_token_amd import rdx
     from prefix_shared_kv_token_amd.runtime import Runtime
 
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     prompts, segs, gens, hot = served_queue(**QUEUE)
-    print(f"\n[gpu] serving {len(prompts)} prompts, pool {POOL}, policy {policy}", flush=True)
+    print(f"\n[gpu] serving {len(prompts)} prompts, pool {POOL}, policy {policy}, matching unit {unit}", flush=True)
     ld = max(len(p) for p in prompts) + T
     rt = Runtime("bf16", HQ, HKV, D, POOL, BATCH, ld)
-    rt.tree = rdx.Tree(POOL, 1, policy)
-    cache = TokenTrieCache(POOL, 1, policy)
+    rt.tree = rdx.Tree(POOL, unit, policy)
+    cache = TokenTrieCache(POOL, unit, policy)
     dev, tdt = rt.device, rt.tdtype
     worst, hits, n_out = 0.0, 0, 0
     for w0 in range(0, len(prompts), WINDOW):
@@ -120,3 +126,5 @@ def test_scheduled_serving_under_eviction(policy):
           f"max abs err {worst:.3g}", flush=True)
     assert st["evictions"] == ost["evictions"] > 0
     assert worst <= 2e-2
+    if unit > 1:
+        assert hits > 0 and hits % unit == 0
