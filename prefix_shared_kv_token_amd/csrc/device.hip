@@ -62,6 +62,24 @@ struct Timing {
   int32_t used = 0;
 } g_timing;
 
+// Adds one launch's four events to the recording state.  On a failed
+// creation the events made so far are destroyed and nothing is added, so
+// the state keeps four events per launch slot.
+hipError_t add_timing_slot() {
+  hipEvent_t x[4];
+  for (int k = 0; k < 4; ++k) {
+    hipError_t e = hipEventCreate(&x[k]);
+    if (e != hipSuccess) {
+      for (int j = 0; j < k; ++j) (void)hipEventDestroy(x[j]);
+      return e;
+    }
+  }
+  g_timing.ev.insert(g_timing.ev.end(), x, x + 4);
+  g_timing.kind.push_back(0);
+  g_timing.has_merge.push_back(0);
+  return hipSuccess;
+}
+
 // Launches the attention kernel and, for plans with split tiles, the merge
 // kernel behind it; while timing is on, each dispatch carries its own events.
 // untimed: never record (the no-allocation entry point creates no events)
@@ -72,14 +90,8 @@ hipError_t launch(KA attn, KM merge, int64_t n_items, int64_t n_merge, hipStream
   if (!untimed && g_timing.on && g_timing.used < g_timing.cap) {
     const int32_t i = g_timing.used;
     while ((int32_t)g_timing.kind.size() <= i) {
-      for (int k = 0; k < 4; ++k) {
-        hipEvent_t x;
-        hipError_t e = hipEventCreate(&x);
-        if (e != hipSuccess) return e;
-        g_timing.ev.push_back(x);
-      }
-      g_timing.kind.push_back(0);
-      g_timing.has_merge.push_back(0);
+      hipError_t e = add_timing_slot();
+      if (e != hipSuccess) return e;
     }
     g_timing.kind[i] = kind;
     g_timing.has_merge[i] = n_merge > 0;
@@ -516,14 +528,8 @@ int rdx_timing_begin(int32_t cap) {
   // records create none (event creation costs the host microseconds per
   // event, which a host-paced launch sequence would otherwise absorb)
   while ((int32_t)g_timing.kind.size() < cap) {
-    for (int k = 0; k < 4; ++k) {
-      hipEvent_t x;
-      hipError_t e = hipEventCreate(&x);
-      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-      g_timing.ev.push_back(x);
-    }
-    g_timing.kind.push_back(0);
-    g_timing.has_merge.push_back(0);
+    hipError_t e = add_timing_slot();
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
   }
   g_timing.on = true;
   g_timing.cap = cap;
