@@ -27,8 +27,11 @@
  *     never allocates or frees device memory (it allocates pinned host
  *     staging memory for plan uploads).
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
- *     Device calls only enqueue work; they do not synchronise.  Faults inside
- *     a kernel surface at the caller's next synchronisation.
+ *     Device calls only enqueue work; they do not synchronise, except where
+ *     stated: a plan upload (and the decode step and job launch that make
+ *     one) waits while the pinned staging buffer it reuses is still being
+ *     read, and rdx_timing_read waits for the launches it reports.  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
  *   - Not thread-safe per object: one thread drives a tree and its plans.
  */
 #ifndef RDX_H
