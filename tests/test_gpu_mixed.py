@@ -4,6 +4,8 @@ against the fp64 oracle.  Matched lengths and page-table rows bit-exact;
 outputs within max-abs 1e-4 (fp32) / 2e-2 (bf16).  The small shapes are
 checked on every output; the full BatchLLM-shaped job (the benchmark's
 configuration) on sampled tokens the oracle computes one by one."""
+import os
+
 import numpy as np
 import pytest
 
@@ -80,7 +82,8 @@ def _random_mixed(seed):
     return cfg, s_chunk, m, int(rng.choice([0, 0, 16, 100000]))
 
 
-@pytest.mark.parametrize("seed", range(12))
+# RDX_RANDOM_SEEDS=N runs seeds 0..N-1 instead (a longer sweep)
+@pytest.mark.parametrize("seed", range(int(os.environ.get("RDX_RANDOM_SEEDS", 12))))
 def test_mixed_random_every_output(seed):
     """Every output and page-table row of a seeded random token-batched job
     through the library's job runner, against the oracle."""

@@ -5,6 +5,8 @@ within max-abs 1e-4 (fp32 workloads) or 2e-2 (bf16 workloads, fp32
 accumulation).  Small shapes are checked on every output; the five full-size
 workloads run exactly as the benchmark runs them and are checked on sampled
 requests the oracle computes one by one."""
+import os
+
 import numpy as np
 import pytest
 
@@ -139,7 +141,8 @@ def _random_case(seed):
     return kw, items, holes
 
 
-@pytest.mark.parametrize("seed", range(32))
+# RDX_RANDOM_SEEDS=N runs seeds 0..N-1 instead (a longer sweep)
+@pytest.mark.parametrize("seed", range(int(os.environ.get("RDX_RANDOM_SEEDS", 32))))
 def test_random_shapes(seed):
     """Every output of a seeded random workload against the oracle."""
     kw, items, (hole_seed, extra) = _random_case(seed)
